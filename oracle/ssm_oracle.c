@@ -1,0 +1,163 @@
+/*
+ * ssm_oracle.c -- fp64 CPU oracle for the Mamba-1 selective scan and the
+ * single-token recurrent state update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product path
+ * (the HIP library and its Python binding) never calls it, and it shares no
+ * code, header or helper with that path.
+ *
+ * What it computes (plain definitions, written as sequential loops):
+ *
+ *   Diagonal (S4D) state space model with zero-order-hold decay and the
+ *   first-order input term used by Mamba:
+ *       abar[t,n] = exp(delta[t] * A[n])                      (decay)
+ *       h[t,n]    = abar[t,n] * h[t-1,n] + delta[t]*B[t,n]*x[t]
+ *       y[t]      = sum_n C[t,n]*h[t,n] + D*x[t]
+ *       y[t]     *= z[t] * sigmoid(z[t])                      (SiLU gate)
+ *   Sources:
+ *     - "Deriving and implementing Mamba from scratch" (dpshk.com/news/3333417),
+ *       section 2.2 (discrete recurrence h_k = Abar h_{k-1} + Bbar x_k,
+ *       y_k = C h_k + D x_k), section 3.2 (diagonal A: Abar = diag(exp(delta a_i)),
+ *       elementwise update h^(i) = exp(delta a_i) h^(i) + delta b_i x),
+ *       section 4.2 (selective Abar_k = exp(delta_k A), Bbar_k = delta_k B(x_k)),
+ *       section 5.1 (SelectiveSSM: B, C of width d_state shared by every channel,
+ *       Bbar = delta*B, state starts at zero, y_t = <h, C_t> + D x_t),
+ *       section 5.2 (MambaBlock: SSM output multiplied by SiLU(gate)).
+ *     - "Mamba from principle to code" (lshu.cn/news/79586), section 3.1
+ *       (B, C have shape (batch, seq_len, d_state); delta = softplus(...) > 0)
+ *       and section 6.5 (state cache shape (batch, d_inner, d_state)).
+ *     - "SSMs for long-document QA" (pwwt.cn/news/5168881), section 3.1
+ *       (segment-wise processing: the final state of one segment is the
+ *       initial state of the next) -- this is the h0 / h_last contract.
+ *     - "State space models vs Transformer: a practical guide"
+ *       (datadaily.news), "How SSMs actually work" (one recurrent step:
+ *       h_new from h, then y_t from h_new) -- the single-token update.
+ *
+ *   Readings taken where the pages are silent or loose:
+ *     - y[t] is read from the state AFTER it absorbed x[t] (h_{-1} = h0);
+ *       h_last is the state after the final step.
+ *     - D == NULL means D = 0; z == NULL means no gate; h0 == NULL means a
+ *       zero initial state; h_last == NULL means it is not written.
+ *     - B and C are indexed [b][t][n] and shared by every channel d.
+ *
+ *   The exact-ZOH input term (input_mode 1) uses the unapproximated
+ *   Bbar = (delta A)^{-1} (exp(delta A) - 1) delta B from section 2.2 of the
+ *   derivation page and section 2.2 of "Mamba from principle to code"; for a
+ *   diagonal A this is (exp(delta a) - 1)/a * B per state.  For a == 0 it is
+ *   the limit delta*B.
+ *
+ *   Delta preprocessing (delta_mode 1) applies the selection step of
+ *   section 4.1 of the derivation page, delta = softplus(raw + bias[d]),
+ *   with softplus(v) = log(1 + exp(v)).
+ *
+ * Arithmetic: IEEE double, libm exp/log1p, no fast-math.  No blocking,
+ * reordering or fusion beyond the loops above.  Single-threaded.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG (-1)
+
+/* softplus(v) = log(1 + exp(v)), written to avoid overflow for large v. */
+static double oracle_softplus(double v) {
+  if (v > 30.0) return v + log1p(exp(-v));
+  return log1p(exp(v));
+}
+
+/*
+ * One channel (b, d) of the scan over t = 0..seqlen-1.
+ * Strides are in elements.  state[] holds h on entry (initial state) and on
+ * exit (final state).
+ */
+static void oracle_scan_channel(const double* x, const double* delta, const double* A_row, const double* B,
+                                const double* C, double Dval, const double* z, double* y, double* state,
+                                int64_t seqlen, int64_t d_state, int64_t io_stride, int64_t bc_stride,
+                                int input_mode, int delta_mode, double dt_bias) {
+  for (int64_t t = 0; t < seqlen; ++t) {
+    double xv = x[t * io_stride];
+    double dt = delta[t * io_stride];
+    if (delta_mode == 1) dt = oracle_softplus(dt + dt_bias);
+    const double* Bt = B + t * bc_stride;
+    const double* Ct = C + t * bc_stride;
+    double acc = 0.0;
+    for (int64_t n = 0; n < d_state; ++n) {
+      double a = A_row[n];
+      double abar = exp(dt * a);
+      double bbar;
+      if (input_mode == 1) {
+        /* exact ZOH for a diagonal entry: (exp(dt a) - 1) / a * B */
+        bbar = (a != 0.0) ? (expm1(dt * a) / a) * Bt[n] : dt * Bt[n];
+      } else {
+        bbar = dt * Bt[n];
+      }
+      state[n] = abar * state[n] + bbar * xv;
+      acc += Ct[n] * state[n];
+    }
+    double yv = acc + Dval * xv;
+    if (z != NULL) {
+      double zv = z[t * io_stride];
+      yv = yv * (zv / (1.0 + exp(-zv)));
+    }
+    y[t * io_stride] = yv;
+  }
+}
+
+/*
+ * Full-sequence selective scan.
+ *   x, delta, z, y : [batch][seqlen][d_inner]
+ *   A              : [d_inner][d_state]
+ *   B, C           : [batch][seqlen][d_state]
+ *   D, dt_bias     : [d_inner]           (nullable)
+ *   h0, h_last     : [batch][d_inner][d_state]  (nullable)
+ * input_mode: 0 = Bbar = delta*B (the simplified term), 1 = exact ZOH.
+ * delta_mode: 0 = delta used as given, 1 = softplus(delta + dt_bias[d]).
+ */
+int ssm_oracle_scan_f64(const double* x, const double* delta, const double* A, const double* B, const double* C,
+                        const double* D, const double* z, const double* h0, const double* dt_bias, double* y,
+                        double* h_last, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                        int input_mode, int delta_mode) {
+  if (!x || !delta || !A || !B || !C || !y) return ORACLE_BAD_ARG;
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0) return ORACLE_BAD_ARG;
+  if (input_mode != 0 && input_mode != 1) return ORACLE_BAD_ARG;
+  if (delta_mode != 0 && delta_mode != 1) return ORACLE_BAD_ARG;
+  if (delta_mode == 1 && !dt_bias) return ORACLE_BAD_ARG;
+  double* state = (double*)malloc((size_t)d_state * sizeof(double));
+  if (!state) return ORACLE_BAD_ARG;
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < d_inner; ++d) {
+      for (int64_t n = 0; n < d_state; ++n)
+        state[n] = h0 ? h0[(b * d_inner + d) * d_state + n] : 0.0;
+      int64_t off = b * seqlen * d_inner + d;
+      oracle_scan_channel(x + off, delta + off, A + d * d_state, B + b * seqlen * d_state,
+                          C + b * seqlen * d_state, D ? D[d] : 0.0, z ? z + off : NULL, y + off, state, seqlen,
+                          d_state, d_inner, d_state, input_mode, delta_mode, dt_bias ? dt_bias[d] : 0.0);
+      if (h_last)
+        for (int64_t n = 0; n < d_state; ++n) h_last[(b * d_inner + d) * d_state + n] = state[n];
+    }
+  }
+  free(state);
+  return ORACLE_OK;
+}
+
+/*
+ * Single-token recurrent update (decode), in place on h.
+ *   h           : [batch][d_inner][d_state]   (in/out)
+ *   x_t, delta_t, z_t, y_t : [batch][d_inner]
+ *   B_t, C_t    : [batch][d_state]
+ * This is the scan body for one step: a scan of length 1 that starts from h
+ * and writes its final state back into h.
+ */
+int ssm_oracle_update_f64(double* h, const double* x_t, const double* delta_t, const double* A, const double* B_t,
+                          const double* C_t, const double* D, const double* z_t, const double* dt_bias, double* y_t,
+                          int64_t batch, int64_t d_inner, int64_t d_state, int input_mode, int delta_mode) {
+  if (!h) return ORACLE_BAD_ARG;
+  /* x_t is [batch][1][d_inner]; B_t is [batch][1][d_state]; h is both h0 and h_last. */
+  return ssm_oracle_scan_f64(x_t, delta_t, A, B_t, C_t, D, z_t, h, dt_bias, y_t, h, batch, 1, d_inner, d_state,
+                             input_mode, delta_mode);
+}
+
+int ssm_oracle_version(void) { return 1; }
