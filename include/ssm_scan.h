@@ -1,0 +1,197 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * Two operations, both from the Mamba selective state space model:
+ *
+ *   ssm_scan_fwd      full-sequence selective scan (training / prefill)
+ *   ssm_state_update  one recurrent step on a resident state (decode)
+ *
+ * Per batch row b, channel d and state n (A diagonal, B and C shared by all
+ * channels of a row):
+ *
+ *   abar[t,n] = exp(delta[b,t,d] * A[d,n])
+ *   h[t,n]    = abar[t,n] * h[t-1,n] + delta[b,t,d] * B[b,t,n] * x[b,t,d]
+ *   y[b,t,d]  = (sum_n C[b,t,n] * h[t,n] + D[d] * x[b,t,d]) * silu(z[b,t,d])
+ *   silu(v)   = v / (1 + exp(-v))
+ *
+ * Sources (web pages; cited by title, address and section):
+ *   - "Deriving and implementing Mamba from scratch" (dpshk.com/news/3333417):
+ *     section 2.2 (discrete recurrence and output equation), section 3.2
+ *     (diagonal A, elementwise update with exp(delta a_i) and delta b_i),
+ *     section 4.2 (Abar_k = exp(delta_k A), Bbar_k = delta_k B(x_k)),
+ *     section 5.1 (B and C of width d_state, shared across channels; state
+ *     starts at zero; y_t = <h_t, C_t> + D x_t), section 5.2 (SSM output
+ *     multiplied by SiLU of the gate branch).
+ *   - "Mamba from principle to code" (lshu.cn/news/79586): section 3.1
+ *     (B, C shaped (batch, seq_len, d_state); delta positive via softplus),
+ *     section 6.5 (decode cache of shape (batch, d_inner, d_state)).
+ *   - "SSMs for long-document QA" (pwwt.cn/news/5168881), section 3.1 (the
+ *     final state of a segment seeds the next segment) and section 3.4
+ *     (per-token state update during serving).
+ *   - "State space models vs Transformer: a practical guide" (datadaily.news),
+ *     "How SSMs actually work": one recurrent step updates the state, then
+ *     reads the output from the new state.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never frees, keeps or allocates them.  It allocates nothing on
+ *     any path and holds no mutable global state; concurrent calls on
+ *     different streams with disjoint outputs are safe.
+ *   - Tensors are dense, row-major (C order), with the shapes given below.
+ *   - io_dtype selects the element type of x, delta, z, B, C and y:
+ *     SSM_DTYPE_F32 (IEEE binary32) or SSM_DTYPE_BF16 (bfloat16, passed as
+ *     raw 16-bit patterns).  A, D, h0, h_last, h and dt_bias are always fp32.
+ *     Arithmetic and the state are fp32 in every case; y is rounded to the
+ *     output type with round-to-nearest-even.
+ *   - stream is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; outputs are valid once the stream has reached the
+ *     enqueue point.
+ *   - Every argument is checked on the host before anything is enqueued.  A
+ *     negative return means nothing was launched and no memory was touched.
+ *     Launch failures reported by HIP return SSM_ERR_HIP.  Values are not
+ *     inspected: NaN and Inf propagate by IEEE rules.
+ *   - A tensor with zero elements may be passed as NULL.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum {
+  SSM_DTYPE_F32 = 0,
+  SSM_DTYPE_BF16 = 1
+} ssm_dtype_t;
+
+enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL_ARG = -1,     /* a required pointer is NULL */
+  SSM_ERR_BAD_DIM = -2,      /* negative size, size overflow, or a grid beyond HIP limits */
+  SSM_ERR_UNSUPPORTED = -3,  /* d_state, dtype, flag or tuning option not supported */
+  SSM_ERR_MISALIGNED = -4,   /* a pointer is not aligned as documented */
+  SSM_ERR_WORKSPACE = -5,    /* workspace missing or smaller than the query returned */
+  SSM_ERR_HIP = -6,          /* the HIP runtime reported an error while launching */
+  SSM_ERR_ALIAS = -7         /* an output overlaps an input it must not overlap */
+};
+
+/* Flags for the extended calls. */
+#define SSM_FLAG_DELTA_SOFTPLUS 0x1u /* delta holds the raw projection; the step used is
+                                        softplus(delta + dt_bias[d]) (selection step,
+                                        derivation page section 4.1; dt_bias required) */
+#define SSM_FLAG_EXACT_ZOH 0x2u      /* input term uses the exact zero-order hold
+                                        Bbar = (exp(delta a) - 1) / a * B per state
+                                        (derivation page section 2.2) instead of delta*B */
+
+/* Returns SSM_ABI_VERSION of the loaded library. */
+int ssm_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* ssm_strerror(int status);
+
+/*
+ * Tuning and variant options for the extended scan.  Zero-initialise for the
+ * defaults (the plain call uses exactly these defaults).
+ *   n_split   : waves that share one 64-channel tile, each owning
+ *               d_state / n_split states (0 = chosen by the library;
+ *               otherwise 1, 2, 4 or 8 with d_state / n_split in {2,4,8,16}).
+ *   chunk_len : timesteps per sequence chunk (0 = chosen by the library).
+ *               When the sequence is split, chunk summaries are combined by an
+ *               associative scan before the chunks are swept with their true
+ *               entry states; results equal the unsplit scan up to fp32
+ *               rounding.
+ *   flags     : SSM_FLAG_* bits.
+ *   dt_bias   : [d_inner] fp32, required with SSM_FLAG_DELTA_SOFTPLUS, else ignored.
+ */
+typedef struct ssm_scan_opts {
+  int32_t n_split;
+  int32_t reserved0;
+  int64_t chunk_len;
+  uint32_t flags;
+  uint32_t reserved1;
+  const float* dt_bias;
+} ssm_scan_opts_t;
+
+/*
+ * Workspace bytes ssm_scan_fwd needs for these sizes (0 when the sequence is
+ * not split).  Returns (size_t)-1 for invalid sizes.  Pure host computation.
+ */
+size_t ssm_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state);
+
+/* Same for ssm_scan_fwd_ex with the given options (opts may be NULL). */
+size_t ssm_scan_fwd_ex_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                      const ssm_scan_opts_t* opts);
+
+/*
+ * The decomposition the library would launch: waves per tile and timesteps
+ * per chunk.  Returns SSM_OK or a negative status for invalid arguments.
+ */
+int ssm_scan_fwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, const ssm_scan_opts_t* opts,
+                      int32_t* n_split_out, int64_t* chunk_len_out, int64_t* n_chunks_out);
+
+/*
+ * Full-sequence selective scan.
+ *
+ *   x, delta, z, y : [batch][seqlen][d_inner]  io_dtype.  delta > 0 is the
+ *                    discretisation step as used (softplus already applied).
+ *   A              : [d_inner][d_state] fp32 (diagonal of the continuous A).
+ *   B, C           : [batch][seqlen][d_state] io_dtype.
+ *   D              : [d_inner] fp32 skip weight, or NULL for D = 0.
+ *   z              : gate input, or NULL for no gate.
+ *   h0             : [batch][d_inner][d_state] fp32 state before t = 0, or NULL for zeros.
+ *   h_last         : [batch][d_inner][d_state] fp32 state after t = seqlen-1, or NULL.
+ *                    h_last may be the same buffer as h0 (resume in place); it
+ *                    must not overlap any other argument.
+ *   y              : must not overlap any input.
+ *   workspace      : device buffer of at least ssm_scan_fwd_workspace_size()
+ *                    bytes, 256-byte aligned (may be NULL when that is 0).
+ *                    Its contents on entry are ignored.
+ *   Alignment      : every pointer aligned to its element size; B and C to 4 bytes.
+ *   d_state        : 2, 4, 8, 16, 32, 64 or 128.
+ *   Sizes          : batch, seqlen, d_inner >= 0 (any of them 0 is a valid
+ *                    empty call; with seqlen 0, h_last receives h0).
+ */
+int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen,
+                 int64_t d_inner, int64_t d_state, int32_t io_dtype, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* ssm_scan_fwd with options (opts may be NULL = defaults). */
+int ssm_scan_fwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                    const void* z, const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen,
+                    int64_t d_inner, int64_t d_state, int32_t io_dtype, const ssm_scan_opts_t* opts,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Single-token recurrent update (decode), in place on h.
+ *
+ *   h        : [batch][d_inner][d_state] fp32, read and overwritten with the new state.
+ *              16-byte aligned when d_state >= 4.
+ *   x_t, delta_t, z_t, y_t : [batch][d_inner] io_dtype (z_t may be NULL: no gate).
+ *   A        : [d_inner][d_state] fp32.
+ *   B_t, C_t : [batch][d_state] io_dtype, 4-byte aligned.
+ *   D        : [d_inner] fp32 or NULL.
+ *   d_state  : 2, 4, 8, 16, 32 or 64.
+ *   y_t must not overlap any input; h must not overlap any other argument.
+ * Equivalent to ssm_scan_fwd with seqlen = 1, h0 = h_last = h.
+ */
+int ssm_state_update(float* h, const void* x_t, const void* delta_t, const float* A, const void* B_t,
+                     const void* C_t, const float* D, const void* z_t, void* y_t, int64_t batch, int64_t d_inner,
+                     int64_t d_state, int32_t io_dtype, void* stream);
+
+/* ssm_state_update with flags (SSM_FLAG_*) and dt_bias (required with
+ * SSM_FLAG_DELTA_SOFTPLUS, else ignored). */
+int ssm_state_update_ex(float* h, const void* x_t, const void* delta_t, const float* A, const void* B_t,
+                        const void* C_t, const float* D, const void* z_t, void* y_t, int64_t batch, int64_t d_inner,
+                        int64_t d_state, int32_t io_dtype, uint32_t flags, const float* dt_bias, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,301 @@
+// C ABI of the selective-scan library: argument checks, launch planning and
+// dispatch to the gfx950 kernels.  Every check runs on the host before any
+// HIP call, so a rejected call has no side effects.
+#include "ssm_scan.h"
+#include "ssm_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+
+namespace ssm {
+int64_t update_grid_blocks(int64_t batch, int64_t d_inner, int32_t d_state);
+}
+
+namespace {
+
+// Target number of resident waves for a full MI355X (256 CUs x 4 SIMDs, two
+// waves per SIMD keep the VALU busy while one waits on memory).
+constexpr int64_t kTargetWaves = 2048;
+// Shortest chunk the automatic plan will cut a sequence into.
+constexpr int64_t kMinAutoChunk = 512;
+// Workspace alignment the library asks for.
+constexpr uintptr_t kWorkspaceAlign = 256;
+
+bool mul3(int64_t a, int64_t b, int64_t c, int64_t* out) {
+  int64_t t;
+  if (__builtin_mul_overflow(a, b, &t)) return false;
+  if (__builtin_mul_overflow(t, c, out)) return false;
+  return true;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Byte ranges [p, p+n) and [q, q+m) overlap (empty ranges never overlap).
+bool overlap(const void* p, int64_t n, const void* q, int64_t m) {
+  if (p == nullptr || q == nullptr || n <= 0 || m <= 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + (uintptr_t)m && b < a + (uintptr_t)n;
+}
+
+struct Plan {
+  int32_t n_split;
+  int64_t chunk_len;
+  int64_t n_chunks;
+};
+
+int make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, const ssm_scan_opts_t* o, Plan* pl) {
+  const int gmin = d_state > 16 ? (int)(d_state / 16) : 1;
+  const int gmax = (int)(d_state / 2) < ssm::kMaxSplit ? (int)(d_state / 2) : ssm::kMaxSplit;
+  if (gmin > gmax) return SSM_ERR_UNSUPPORTED;
+  const int64_t tiles = (d_inner + 63) / 64;
+  const int64_t base = batch * tiles;
+  int g;
+  if (o != nullptr && o->n_split != 0) {
+    g = o->n_split;
+    if (!is_pow2(g) || g < gmin || g > gmax) return SSM_ERR_UNSUPPORTED;
+  } else {
+    g = gmin;
+    while (g < gmax && base * g < kTargetWaves) g *= 2;
+  }
+  int64_t chunk_len;
+  if (o != nullptr && o->chunk_len < 0) return SSM_ERR_UNSUPPORTED;
+  if (o != nullptr && o->chunk_len > 0) {
+    chunk_len = o->chunk_len;
+  } else {
+    int64_t nch = 1;
+    const int64_t waves = base * g;
+    if (waves > 0 && waves * 2 <= kTargetWaves && seqlen >= 2 * kMinAutoChunk) {
+      nch = (kTargetWaves + waves - 1) / waves;
+      if (nch > seqlen / kMinAutoChunk) nch = seqlen / kMinAutoChunk;
+    }
+    chunk_len = (seqlen + nch - 1) / nch;
+    chunk_len = (chunk_len + ssm::kTimeBlock - 1) / ssm::kTimeBlock * ssm::kTimeBlock;
+  }
+  if (chunk_len <= 0) chunk_len = 1;
+  if (chunk_len > seqlen && seqlen > 0) chunk_len = seqlen;
+  pl->n_split = g;
+  pl->chunk_len = chunk_len;
+  pl->n_chunks = seqlen > 0 ? (seqlen + chunk_len - 1) / chunk_len : 1;
+  return SSM_OK;
+}
+
+bool scan_d_state_ok(int64_t n) { return n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64 || n == 128; }
+bool update_d_state_ok(int64_t n) { return n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64; }
+
+int check_dims(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0) return SSM_ERR_BAD_DIM;
+  return SSM_OK;
+}
+
+int workspace_bytes_for(int64_t batch, int64_t d_inner, int64_t d_state, const Plan& pl, size_t* out) {
+  int64_t states;
+  if (!mul3(batch, d_inner, d_state, &states)) return SSM_ERR_BAD_DIM;
+  const int64_t nch = pl.n_chunks;
+  int64_t floats;
+  if (nch <= 1) {
+    floats = 0;
+  } else if (__builtin_mul_overflow(3 * nch - 2, states, &floats)) {
+    return SSM_ERR_BAD_DIM;
+  }
+  int64_t bytes;
+  if (__builtin_mul_overflow(floats, (int64_t)sizeof(float), &bytes)) return SSM_ERR_BAD_DIM;
+  *out = (size_t)bytes;
+  return SSM_OK;
+}
+
+int scan_impl(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+              const void* z, const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen,
+              int64_t d_inner, int64_t d_state, int32_t io_dtype, const ssm_scan_opts_t* opts, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  int rc = check_dims(batch, seqlen, d_inner, d_state);
+  if (rc != SSM_OK) return rc;
+  if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
+  if (!scan_d_state_ok(d_state)) return SSM_ERR_UNSUPPORTED;
+  if (opts != nullptr && opts->flags != 0) return SSM_ERR_UNSUPPORTED;
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+
+  int64_t n_io, n_bc, n_h, n_a;
+  if (!mul3(batch, seqlen, d_inner, &n_io) || !mul3(batch, seqlen, d_state, &n_bc) ||
+      !mul3(batch, d_inner, d_state, &n_h) || !mul3(1, d_inner, d_state, &n_a))
+    return SSM_ERR_BAD_DIM;
+  int64_t b_io, b_bc, b_h, b_a;
+  if (__builtin_mul_overflow(n_io, es, &b_io) || __builtin_mul_overflow(n_bc, es, &b_bc) ||
+      __builtin_mul_overflow(n_h, (int64_t)4, &b_h) || __builtin_mul_overflow(n_a, (int64_t)4, &b_a))
+    return SSM_ERR_BAD_DIM;
+  const int64_t b_d = d_inner * 4;
+
+  // Required pointers (a tensor with no elements may be NULL).
+  if (n_io > 0 && (x == nullptr || delta == nullptr || y == nullptr)) return SSM_ERR_NULL_ARG;
+  if (n_bc > 0 && n_io > 0 && (B == nullptr || C == nullptr)) return SSM_ERR_NULL_ARG;
+  if (n_a > 0 && n_io > 0 && A == nullptr) return SSM_ERR_NULL_ARG;
+
+  // Alignment.
+  if (!aligned(x, es) || !aligned(delta, es) || !aligned(z, es) || !aligned(y, es)) return SSM_ERR_MISALIGNED;
+  if (!aligned(B, 4) || !aligned(C, 4) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) || !aligned(h_last, 4))
+    return SSM_ERR_MISALIGNED;
+
+  // Aliasing: y overlaps nothing; h_last overlaps nothing except h0 exactly.
+  const void* ins[] = {x, delta, z, B, C, A, D, h0};
+  const int64_t inb[] = {b_io, b_io, z ? b_io : 0, b_bc, b_bc, b_a, D ? b_d : 0, h0 ? b_h : 0};
+  for (int k = 0; k < 8; ++k)
+    if (overlap(y, b_io, ins[k], inb[k])) return SSM_ERR_ALIAS;
+  if (overlap(y, b_io, h_last, h_last ? b_h : 0)) return SSM_ERR_ALIAS;
+  if (h_last != nullptr) {
+    for (int k = 0; k < 7; ++k)
+      if (overlap(h_last, b_h, ins[k], inb[k])) return SSM_ERR_ALIAS;
+    if (h0 != nullptr && h0 != h_last && overlap(h_last, b_h, h0, b_h)) return SSM_ERR_ALIAS;
+  }
+
+  Plan pl;
+  rc = make_plan(batch, seqlen, d_inner, d_state, opts, &pl);
+  if (rc != SSM_OK) return rc;
+  size_t need;
+  rc = workspace_bytes_for(batch, d_inner, d_state, pl, &need);
+  if (rc != SSM_OK) return rc;
+  const int64_t tiles = (d_inner + 63) / 64;
+  int64_t grid;
+  if (!mul3(batch, pl.n_chunks, tiles, &grid) || grid > INT32_MAX) return SSM_ERR_BAD_DIM;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+    if (!aligned(workspace, kWorkspaceAlign)) return SSM_ERR_MISALIGNED;
+    const void* all[] = {x, delta, z, B, C, A, D, h0, y, h_last};
+    const int64_t allb[] = {b_io, b_io, z ? b_io : 0, b_bc, b_bc, b_a, D ? b_d : 0, h0 ? b_h : 0, b_io,
+                            h_last ? b_h : 0};
+    for (int k = 0; k < 10; ++k)
+      if (overlap(workspace, (int64_t)need, all[k], allb[k])) return SSM_ERR_ALIAS;
+  }
+  int64_t state_blocks = (n_h + 255) / 256;
+  if (state_blocks > INT32_MAX) return SSM_ERR_BAD_DIM;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch == 0 || d_inner == 0) return SSM_OK;
+  if (seqlen == 0) {
+    if (h_last == nullptr || h_last == h0) return SSM_OK;
+    return ssm::launch_state_fill(h_last, h0, n_h, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
+  ssm::ScanLaunch p{x, delta, A, B, C, D, z, h0, y, h_last, static_cast<float*>(workspace), batch, seqlen, d_inner,
+                    (int32_t)d_state, pl.n_split, pl.chunk_len, pl.n_chunks, io_dtype == SSM_DTYPE_BF16, s};
+  return ssm::launch_scan(p) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int update_impl(float* h, const void* x_t, const void* delta_t, const float* A, const void* B_t, const void* C_t,
+                const float* D, const void* z_t, void* y_t, int64_t batch, int64_t d_inner, int64_t d_state,
+                int32_t io_dtype, uint32_t flags, const float* dt_bias, void* stream) {
+  (void)dt_bias;
+  if (batch < 0 || d_inner < 0 || d_state <= 0) return SSM_ERR_BAD_DIM;
+  if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
+  if (!update_d_state_ok(d_state)) return SSM_ERR_UNSUPPORTED;
+  if (flags != 0) return SSM_ERR_UNSUPPORTED;
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  int64_t n_io, n_h, n_bc;
+  if (!mul3(batch, d_inner, 1, &n_io) || !mul3(batch, d_inner, d_state, &n_h) || !mul3(batch, d_state, 1, &n_bc))
+    return SSM_ERR_BAD_DIM;
+  int64_t b_io, b_h, b_bc, b_a;
+  if (__builtin_mul_overflow(n_io, es, &b_io) || __builtin_mul_overflow(n_h, (int64_t)4, &b_h) ||
+      __builtin_mul_overflow(n_bc, es, &b_bc) || __builtin_mul_overflow(d_inner * d_state, (int64_t)4, &b_a))
+    return SSM_ERR_BAD_DIM;
+  if (n_io > 0 && (h == nullptr || x_t == nullptr || delta_t == nullptr || y_t == nullptr || A == nullptr ||
+                   B_t == nullptr || C_t == nullptr))
+    return SSM_ERR_NULL_ARG;
+  const uintptr_t ha = d_state >= 4 ? 16 : 8;
+  if (!aligned(h, ha) || !aligned(A, ha)) return SSM_ERR_MISALIGNED;
+  if (!aligned(x_t, es) || !aligned(delta_t, es) || !aligned(z_t, es) || !aligned(y_t, es)) return SSM_ERR_MISALIGNED;
+  if (!aligned(B_t, io_dtype == SSM_DTYPE_BF16 ? 4 : ha) || !aligned(C_t, io_dtype == SSM_DTYPE_BF16 ? 4 : ha) ||
+      !aligned(D, 4))
+    return SSM_ERR_MISALIGNED;
+  const void* ins[] = {x_t, delta_t, z_t, B_t, C_t, A, D};
+  const int64_t inb[] = {b_io, b_io, z_t ? b_io : 0, b_bc, b_bc, b_a, D ? d_inner * 4 : 0};
+  for (int k = 0; k < 7; ++k) {
+    if (overlap(y_t, b_io, ins[k], inb[k])) return SSM_ERR_ALIAS;
+    if (overlap(h, b_h, ins[k], inb[k])) return SSM_ERR_ALIAS;
+  }
+  if (overlap(h, b_h, y_t, b_io)) return SSM_ERR_ALIAS;
+  if (ssm::update_grid_blocks(batch, d_inner, (int32_t)d_state) > INT32_MAX) return SSM_ERR_BAD_DIM;
+  if (n_io == 0) return SSM_OK;
+  ssm::UpdateLaunch p{h, x_t, delta_t, A, B_t, C_t, D, z_t, y_t, batch, d_inner, (int32_t)d_state,
+                      io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream)};
+  return ssm::launch_update(p) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_strerror(int status) {
+  switch (status) {
+    case SSM_OK: return "success";
+    case SSM_ERR_NULL_ARG: return "a required pointer is NULL";
+    case SSM_ERR_BAD_DIM: return "invalid size (negative, overflowing, or beyond launch limits)";
+    case SSM_ERR_UNSUPPORTED: return "unsupported d_state, dtype, flag or option";
+    case SSM_ERR_MISALIGNED: return "pointer not aligned as required";
+    case SSM_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSM_ERR_HIP: return "HIP runtime error while launching";
+    case SSM_ERR_ALIAS: return "an output overlaps an input it must not overlap";
+    default: return "unknown status";
+  }
+}
+
+size_t ssm_scan_fwd_ex_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                      const ssm_scan_opts_t* opts) {
+  if (check_dims(batch, seqlen, d_inner, d_state) != SSM_OK || !scan_d_state_ok(d_state)) return (size_t)-1;
+  Plan pl;
+  if (make_plan(batch, seqlen, d_inner, d_state, opts, &pl) != SSM_OK) return (size_t)-1;
+  size_t need;
+  if (workspace_bytes_for(batch, d_inner, d_state, pl, &need) != SSM_OK) return (size_t)-1;
+  return need;
+}
+
+size_t ssm_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  return ssm_scan_fwd_ex_workspace_size(batch, seqlen, d_inner, d_state, nullptr);
+}
+
+int ssm_scan_fwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, const ssm_scan_opts_t* opts,
+                      int32_t* n_split_out, int64_t* chunk_len_out, int64_t* n_chunks_out) {
+  int rc = check_dims(batch, seqlen, d_inner, d_state);
+  if (rc != SSM_OK) return rc;
+  if (!scan_d_state_ok(d_state)) return SSM_ERR_UNSUPPORTED;
+  Plan pl;
+  rc = make_plan(batch, seqlen, d_inner, d_state, opts, &pl);
+  if (rc != SSM_OK) return rc;
+  if (n_split_out) *n_split_out = pl.n_split;
+  if (chunk_len_out) *chunk_len_out = pl.chunk_len;
+  if (n_chunks_out) *n_chunks_out = pl.n_chunks;
+  return SSM_OK;
+}
+
+int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen,
+                 int64_t d_inner, int64_t d_state, int32_t io_dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return scan_impl(x, delta, A, B, C, D, z, h0, y, h_last, batch, seqlen, d_inner, d_state, io_dtype, nullptr,
+                   workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_fwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                    const void* z, const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen,
+                    int64_t d_inner, int64_t d_state, int32_t io_dtype, const ssm_scan_opts_t* opts,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_impl(x, delta, A, B, C, D, z, h0, y, h_last, batch, seqlen, d_inner, d_state, io_dtype, opts,
+                   workspace, workspace_bytes, stream);
+}
+
+int ssm_state_update(float* h, const void* x_t, const void* delta_t, const float* A, const void* B_t,
+                     const void* C_t, const float* D, const void* z_t, void* y_t, int64_t batch, int64_t d_inner,
+                     int64_t d_state, int32_t io_dtype, void* stream) {
+  return update_impl(h, x_t, delta_t, A, B_t, C_t, D, z_t, y_t, batch, d_inner, d_state, io_dtype, 0, nullptr,
+                     stream);
+}
+
+int ssm_state_update_ex(float* h, const void* x_t, const void* delta_t, const float* A, const void* B_t,
+                        const void* C_t, const float* D, const void* z_t, void* y_t, int64_t batch, int64_t d_inner,
+                        int64_t d_state, int32_t io_dtype, uint32_t flags, const float* dt_bias, void* stream) {
+  return update_impl(h, x_t, delta_t, A, B_t, C_t, D, z_t, y_t, batch, d_inner, d_state, io_dtype, flags, dt_bias,
+                     stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+// Single-token recurrent state update (decode) for gfx950.
+//
+// For each batch row b and channel d, with the state h[b,d,:] resident in HBM:
+//   h[n] <- exp(delta*A[d,n]) * h[n] + delta * B[b,n] * x
+//   y     = (sum_n C[b,n] * h[n] + D[d] * x) * silu(z)
+// One recurrent step of the diagonal selective SSM: "State space models vs
+// Transformer: a practical guide" (datadaily.news), "How SSMs actually work";
+// state shape (batch, d_inner, d_state) from "Mamba from principle to code"
+// (lshu.cn/news/79586) section 6.5; the update itself is section 3.2 of
+// "Deriving and implementing Mamba from scratch" (dpshk.com/news/3333417).
+//
+// The step moves 2 x 4 x d_state bytes of state per channel and a few bytes
+// of io, against ~6 VALU slots per state: it is HBM-bound.  The layout is
+// chosen for the memory system:
+//   * LPC lanes share one channel, each owning 4 consecutive states, so one
+//     wave's 16-byte state loads cover 1 KiB of contiguous memory (fully
+//     coalesced, no partial cache lines per instruction).
+//   * The readout is reduced across the LPC lanes with DPP / swizzle moves;
+//     every lane of the group then holds y, and the first one stores it.
+//   * x, delta, z are read once per lane group (the group's lanes hit the same
+//     cache line); B and C rows are tiny and shared by the whole row.
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+#include <tuple>
+#include <utility>
+
+namespace ssm {
+namespace {
+
+constexpr int kUpdBlock = 256;
+
+// Sum over aligned groups of LPC lanes (LPC a power of two <= 16).
+template <int LPC>
+__device__ __forceinline__ float group_sum(float v) {
+  if (LPC >= 2)  // quad_perm [1,0,3,2]: partner lane ^ 1
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  if (LPC >= 4)  // quad_perm [2,3,0,1]: partner lane ^ 2
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  if (LPC >= 8)  // ds_swizzle bit mode: and 0x1F, xor 4
+    v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x101F));
+  if (LPC >= 16)  // xor 8
+    v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x201F));
+  return v;
+}
+
+template <typename T, int SPL>
+struct LaneStates;
+
+template <>
+struct LaneStates<float, 4> {
+  static __device__ __forceinline__ void load(const float* p, float (&v)[4]) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&v)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+template <>
+struct LaneStates<float, 2> {
+  static __device__ __forceinline__ void load(const float* p, float (&v)[2]) {
+    const float2 q = *reinterpret_cast<const float2*>(p);
+    v[0] = q.x; v[1] = q.y;
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&v)[2]) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  }
+};
+
+// SPL values of a B or C row as fp32 (bf16 pairs are read as dwords).
+template <int SPL>
+__device__ __forceinline__ void load_row(const uint16_t* p, float (&v)[SPL]) {
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+  for (int k = 0; k < SPL / 2; ++k) {
+    const uint32_t w = q[k];
+    v[2 * k] = __builtin_bit_cast(float, w << 16);
+    v[2 * k + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
+  }
+}
+template <int SPL>
+__device__ __forceinline__ void load_row(const float* p, float (&v)[SPL]) {
+  float tmp[SPL];
+  LaneStates<float, SPL>::load(p, tmp);
+#pragma unroll
+  for (int k = 0; k < SPL; ++k) v[k] = tmp[k];
+}
+
+template <typename T, int SPL, int LPC>
+__global__ void __launch_bounds__(kUpdBlock)
+    k_state_update(float* __restrict__ h, const T* __restrict__ x, const T* __restrict__ delta,
+                   const float* __restrict__ A, const T* __restrict__ B, const T* __restrict__ C,
+                   const float* __restrict__ D, const T* __restrict__ z, T* __restrict__ y, int64_t d_inner,
+                   int32_t blocks_per_row) {
+  constexpr int N = SPL * LPC;
+  constexpr int kChan = kUpdBlock / LPC;  // channels per workgroup
+  const int64_t b = blockIdx.x / blocks_per_row;
+  const int blk = blockIdx.x % blocks_per_row;
+  const int sub = threadIdx.x % LPC;
+  const int64_t d = (int64_t)blk * kChan + threadIdx.x / LPC;
+  const bool valid = d < d_inner;
+  const int64_t dc = valid ? d : d_inner - 1;
+  const int s0 = sub * SPL;
+
+  float* hp = h + (b * d_inner + dc) * N + s0;
+  float hv[SPL], al[SPL], Bv[SPL], Cv[SPL];
+  LaneStates<float, SPL>::load(hp, hv);
+  LaneStates<float, SPL>::load(A + dc * N + s0, al);
+  load_row<SPL>(B + b * N + s0, Bv);
+  load_row<SPL>(C + b * N + s0, Cv);
+  const int64_t io = b * d_inner + dc;
+  const float xv = io_to_f32(x[io]);
+  const float dv = io_to_f32(delta[io]);
+  const float wx = dv * xv;
+  float acc = 0.f;
+#pragma unroll
+  for (int n = 0; n < SPL; ++n) {
+    const float ab = hw_exp2(dv * (al[n] * kLog2e));
+    hv[n] = __builtin_fmaf(ab, hv[n], wx * Bv[n]);
+    acc = __builtin_fmaf(Cv[n], hv[n], acc);
+  }
+  acc = group_sum<LPC>(acc);
+  if (valid) {
+    LaneStates<float, SPL>::store(hp, hv);
+    if (sub == 0) {
+      float v = acc;
+      if (D != nullptr) v = __builtin_fmaf(D[dc], xv, v);
+      if (z != nullptr) v *= silu(io_to_f32(z[io]));
+      io_store(y + io, v);
+    }
+  }
+}
+
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t s, Args&&... args) {
+  std::tuple<KArgs...> vals(std::forward<Args>(args)...);
+  void* ptrs[sizeof...(KArgs)];
+  std::apply([&](auto&... v) {
+    int k = 0;
+    ((ptrs[k++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, s);
+}
+
+template <typename T, int SPL, int LPC>
+hipError_t launch_update_t(const UpdateLaunch& p) {
+  constexpr int kChan = kUpdBlock / LPC;
+  const int64_t per_row = (p.d_inner + kChan - 1) / kChan;
+  return launch(k_state_update<T, SPL, LPC>, dim3((unsigned)(p.batch * per_row)), dim3(kUpdBlock), 0, p.stream, p.h,
+                static_cast<const T*>(p.x), static_cast<const T*>(p.delta), p.A, static_cast<const T*>(p.B),
+                static_cast<const T*>(p.C), p.D, static_cast<const T*>(p.z), static_cast<T*>(p.y), p.d_inner,
+                (int32_t)per_row);
+}
+
+template <typename T>
+hipError_t launch_update_n(const UpdateLaunch& p) {
+  switch (p.d_state) {
+    case 2: return launch_update_t<T, 2, 1>(p);
+    case 4: return launch_update_t<T, 4, 1>(p);
+    case 8: return launch_update_t<T, 4, 2>(p);
+    case 16: return launch_update_t<T, 4, 4>(p);
+    case 32: return launch_update_t<T, 4, 8>(p);
+    case 64: return launch_update_t<T, 4, 16>(p);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int64_t update_grid_blocks(int64_t batch, int64_t d_inner, int32_t d_state) {
+  const int lpc = d_state <= 4 ? 1 : d_state / 4;
+  const int64_t chan = kUpdBlock / lpc;
+  return batch * ((d_inner + chan - 1) / chan);
+}
+
+hipError_t launch_update(const UpdateLaunch& p) {
+  return p.bf16 ? launch_update_n<uint16_t>(p) : launch_update_n<float>(p);
+}
+
+}  // namespace ssm

@@ -1,0 +1,223 @@
+"""Seeded synthetic inputs for the selective scan and the decode update.
+
+This module is shared by the device path, the tests and the benchmark; it
+holds none of the scan's arithmetic.  It draws random tensors with the
+distributions of a freshly initialised Mamba layer and rounds them to the
+element type the library receives.
+
+Recipe (the same for every consumer):
+  * ``numpy.random.SeedSequence(seed).spawn(7)`` gives one child per tensor,
+    in the order [dt_bias, x, z, delta-noise, B, C, h0].
+  * dt_bias[d] ~ U[1e-3, 1e-1] (linear-uniform, one value per channel,
+    fixed across batch, time and decode steps).  Step
+    delta = softplus(0.5 * N(0,1) + inv_softplus(dt_bias[d])) with
+    softplus(v) = log(1 + e^v), inv_softplus(u) = log(e^u - 1); the noise is
+    per element.  (Selection step with a positive step size and its
+    initialisation range: "Deriving and implementing Mamba from scratch"
+    (dpshk.com/news/3333417) section 4.1; "SSMs for long-document QA"
+    (pwwt.cn/news/5168881) section 3.3.)
+  * x, z, B, C ~ N(0, 1) per element.
+  * A[d, n] = -(n + 1) for every channel (S4D-real initialisation: A_log =
+    log(1..N), A = -exp(A_log); "Mamba from principle to code"
+    (lshu.cn/news/79586) section 6.2, derivation page section 5.1).
+  * D[d] = 1 (derivation page section 5.1).
+  * h0 ~ N(0, 0.1^2) per state when a nonzero initial state is asked for.
+  * Values are drawn and computed in float64, rounded to float32 (nearest
+    even), and for bf16 tensors rounded again to bfloat16 (nearest even).
+    bf16 tensors are returned as their raw 16-bit patterns (numpy.uint16).
+  * Scan tensors are drawn per (batch row, segment of 4096 timesteps): the
+    tensor's child is spawned into batch * ceil(seqlen / 4096) grandchildren
+    in row-major (row, segment) order, each filling its (segment, d) block in
+    C order.  Decode tensors are drawn per step: the child is spawned into
+    ``steps`` grandchildren, each filling one (batch, width) slab.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+
+SEGMENT = 4096
+_ORDER = ("dt_bias", "x", "z", "delta_noise", "B", "C", "h0")
+
+
+@dataclass(frozen=True)
+class ScanConfig:
+    name: str
+    batch: int
+    seqlen: int
+    d_inner: int
+    d_state: int
+    dtype: str  # "f32" or "bf16"
+    nonzero_h0: bool
+    seed: int
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    batch: int
+    d_inner: int
+    d_state: int
+    dtype: str
+    steps: int
+    seed: int
+
+
+# Layer shapes the library is measured on (seed = position in this list).
+TINY = ScanConfig("tiny", 2, 64, 32, 16, "f32", False, 0)
+MAMBA_130M = ScanConfig("mamba-130m-layer", 8, 2048, 1536, 16, "bf16", False, 1)
+MAMBA_1P4B = ScanConfig("mamba-1.4b-layer", 32, 4096, 4096, 16, "bf16", False, 2)
+MAMBA_2P8B_LONG = ScanConfig("mamba-2.8b-long-layer", 4, 32768, 5120, 16, "bf16", True, 3)
+DECODE = DecodeConfig("decode-256x5120", 256, 5120, 16, "bf16", 1000, 4)
+
+SCAN_CONFIGS = {c.name: c for c in (TINY, MAMBA_130M, MAMBA_1P4B, MAMBA_2P8B_LONG)}
+
+
+def round_to_f32(a: np.ndarray) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64).astype(np.float32)
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); raw uint16 bits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _to_io(a64: np.ndarray, dtype: str) -> np.ndarray:
+    f = round_to_f32(a64)
+    return f32_to_bf16_bits(f) if dtype == "bf16" else f
+
+
+def _softplus(v: np.ndarray) -> np.ndarray:
+    return np.logaddexp(0.0, v)
+
+
+def _inv_softplus(u: np.ndarray) -> np.ndarray:
+    return np.log(np.expm1(u))
+
+
+def _threads(threads: Optional[int]) -> int:
+    if threads:
+        return threads
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def make_scan_inputs(batch: int, seqlen: int, d_inner: int, d_state: int, dtype: str, seed: int,
+                     nonzero_h0: bool = False, threads: Optional[int] = None,
+                     raw_delta: bool = False) -> Dict[str, np.ndarray]:
+    """Host tensors for one scan call.
+
+    Returns x, delta, z (batch, seqlen, d_inner), B, C (batch, seqlen, d_state)
+    in the io type; A (d_inner, d_state), D (d_inner,), dt_bias (d_inner,) fp32;
+    h0 (batch, d_inner, d_state) fp32 or None.  With ``raw_delta`` the
+    returned ``delta`` is the pre-activation 0.5*noise (io type) and
+    ``dt_bias`` is inv_softplus(U) (fp32), so that softplus(delta + dt_bias)
+    is the step; otherwise ``delta`` is the step itself and ``dt_bias`` the
+    uniform draw.
+    """
+    assert dtype in ("f32", "bf16")
+    kids = dict(zip(_ORDER, np.random.SeedSequence(seed).spawn(len(_ORDER))))
+    u = np.random.default_rng(kids["dt_bias"]).uniform(1e-3, 1e-1, size=d_inner)
+    inv_sp = _inv_softplus(u)
+    nseg = max(1, -(-seqlen // SEGMENT))
+    io_t = np.uint16 if dtype == "bf16" else np.float32
+    out = {k: np.empty((batch, seqlen, d_inner), dtype=io_t) for k in ("x", "z", "delta")}
+    out["B"] = np.empty((batch, seqlen, d_state), dtype=io_t)
+    out["C"] = np.empty((batch, seqlen, d_state), dtype=io_t)
+    grand = {k: kids[k].spawn(batch * nseg) for k in ("x", "z", "delta_noise", "B", "C")}
+
+    def fill(task: int):
+        b, s = divmod(task, nseg)
+        t0, t1 = s * SEGMENT, min(seqlen, (s + 1) * SEGMENT)
+        n = t1 - t0
+        if n <= 0:
+            return
+        for k in ("x", "z"):
+            out[k][b, t0:t1] = _to_io(np.random.default_rng(grand[k][task]).standard_normal((n, d_inner)), dtype)
+        noise = np.random.default_rng(grand["delta_noise"][task]).standard_normal((n, d_inner))
+        if raw_delta:
+            out["delta"][b, t0:t1] = _to_io(0.5 * noise, dtype)
+        else:
+            out["delta"][b, t0:t1] = _to_io(_softplus(0.5 * noise + inv_sp[None, :]), dtype)
+        for k in ("B", "C"):
+            out[k][b, t0:t1] = _to_io(np.random.default_rng(grand[k][task]).standard_normal((n, d_state)), dtype)
+
+    tasks = batch * nseg
+    if tasks > 1 and batch * seqlen * d_inner > (1 << 20):
+        with ThreadPoolExecutor(_threads(threads)) as ex:
+            list(ex.map(fill, range(tasks)))
+    else:
+        for t in range(tasks):
+            fill(t)
+    out["A"] = np.ascontiguousarray(
+        np.broadcast_to(-(np.arange(1, d_state + 1, dtype=np.float64)), (d_inner, d_state))).astype(np.float32)
+    out["D"] = np.ones(d_inner, dtype=np.float32)
+    out["dt_bias"] = round_to_f32(inv_sp) if raw_delta else round_to_f32(u)
+    if nonzero_h0:
+        out["h0"] = round_to_f32(0.1 * np.random.default_rng(kids["h0"]).standard_normal((batch, d_inner, d_state)))
+    else:
+        out["h0"] = None
+    return out
+
+
+def scan_inputs(cfg: ScanConfig, threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    return make_scan_inputs(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, cfg.seed, cfg.nonzero_h0,
+                            threads)
+
+
+def make_decode_inputs(batch: int, d_inner: int, d_state: int, dtype: str, steps: int, seed: int,
+                       threads: Optional[int] = None, raw_delta: bool = False) -> Dict[str, np.ndarray]:
+    """Host tensors for ``steps`` consecutive decode steps.
+
+    x, delta, z: (steps, batch, d_inner); B, C: (steps, batch, d_state) in the
+    io type; A (d_inner, d_state), D, dt_bias (d_inner,) fp32; the state
+    starts at zero.
+    """
+    kids = dict(zip(_ORDER, np.random.SeedSequence(seed).spawn(len(_ORDER))))
+    u = np.random.default_rng(kids["dt_bias"]).uniform(1e-3, 1e-1, size=d_inner)
+    inv_sp = _inv_softplus(u)
+    io_t = np.uint16 if dtype == "bf16" else np.float32
+    out = {k: np.empty((steps, batch, d_inner), dtype=io_t) for k in ("x", "z", "delta")}
+    out["B"] = np.empty((steps, batch, d_state), dtype=io_t)
+    out["C"] = np.empty((steps, batch, d_state), dtype=io_t)
+    grand = {k: kids[k].spawn(steps) for k in ("x", "z", "delta_noise", "B", "C")}
+
+    def fill(s: int):
+        for k in ("x", "z"):
+            out[k][s] = _to_io(np.random.default_rng(grand[k][s]).standard_normal((batch, d_inner)), dtype)
+        noise = np.random.default_rng(grand["delta_noise"][s]).standard_normal((batch, d_inner))
+        if raw_delta:
+            out["delta"][s] = _to_io(0.5 * noise, dtype)
+        else:
+            out["delta"][s] = _to_io(_softplus(0.5 * noise + inv_sp[None, :]), dtype)
+        for k in ("B", "C"):
+            out[k][s] = _to_io(np.random.default_rng(grand[k][s]).standard_normal((batch, d_state)), dtype)
+
+    if steps > 1 and steps * batch * d_inner > (1 << 20):
+        with ThreadPoolExecutor(_threads(threads)) as ex:
+            list(ex.map(fill, range(steps)))
+    else:
+        for s in range(steps):
+            fill(s)
+    out["A"] = np.ascontiguousarray(
+        np.broadcast_to(-(np.arange(1, d_state + 1, dtype=np.float64)), (d_inner, d_state))).astype(np.float32)
+    out["D"] = np.ones(d_inner, dtype=np.float32)
+    out["dt_bias"] = round_to_f32(inv_sp) if raw_delta else round_to_f32(u)
+    return out
+
+
+def decode_inputs(cfg: DecodeConfig, steps: Optional[int] = None, threads: Optional[int] = None):
+    return make_decode_inputs(cfg.batch, cfg.d_inner, cfg.d_state, cfg.dtype, steps or cfg.steps, cfg.seed, threads)

@@ -1,0 +1,128 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_84_amd import binding as bd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ssm_scan.h")
+
+# Fake but well-aligned device addresses: validation fails before any use.
+P0 = 0x7F0000000000
+MB = 1 << 20
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(bd.SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_messages(lib):
+    assert bd.abi_version() == 1
+    for code in range(-7, 1):
+        assert bd.strerror(code)
+    assert "unknown" in bd.strerror(-99)
+
+
+def _scan(lib, x=P0, delta=P0 + MB, A=P0 + 2 * MB, B=P0 + 3 * MB, C=P0 + 4 * MB, D=None, z=None, h0=None,
+          y=P0 + 8 * MB, h_last=None, batch=2, L=4, d=8, N=16, dtype=1, opts=None, ws=None, ws_bytes=0):
+    o = ctypes.byref(opts) if opts is not None else None
+    return lib.ssm_scan_fwd_ex(x, delta, A, B, C, D, z, h0, y, h_last, batch, L, d, N, dtype, o, ws, ws_bytes, None)
+
+
+def test_scan_argument_errors(lib):
+    assert _scan(lib, x=None) == bd.SSM_ERR_NULL_ARG
+    assert _scan(lib, y=None) == bd.SSM_ERR_NULL_ARG
+    assert _scan(lib, B=None) == bd.SSM_ERR_NULL_ARG
+    assert _scan(lib, A=None) == bd.SSM_ERR_NULL_ARG
+    assert _scan(lib, batch=-1) == bd.SSM_ERR_BAD_DIM
+    assert _scan(lib, L=-3) == bd.SSM_ERR_BAD_DIM
+    assert _scan(lib, N=0) == bd.SSM_ERR_BAD_DIM
+    assert _scan(lib, N=3) == bd.SSM_ERR_UNSUPPORTED
+    assert _scan(lib, N=256) == bd.SSM_ERR_UNSUPPORTED
+    assert _scan(lib, dtype=7) == bd.SSM_ERR_UNSUPPORTED
+    assert _scan(lib, batch=1 << 40, L=1 << 20, d=1 << 10) == bd.SSM_ERR_BAD_DIM
+    assert _scan(lib, x=P0 + 1) == bd.SSM_ERR_MISALIGNED
+    assert _scan(lib, dtype=0, delta=P0 + MB + 2) == bd.SSM_ERR_MISALIGNED
+    assert _scan(lib, B=P0 + 3 * MB + 2) == bd.SSM_ERR_MISALIGNED
+    assert _scan(lib, h0=P0 + 9 * MB + 2) == bd.SSM_ERR_MISALIGNED
+    # y overlapping an input, h_last overlapping x, h_last partially over h0.
+    assert _scan(lib, y=P0 + 16) == bd.SSM_ERR_ALIAS
+    assert _scan(lib, h_last=P0 + 64) == bd.SSM_ERR_ALIAS
+    assert _scan(lib, h0=P0 + 9 * MB, h_last=P0 + 9 * MB + 64) == bd.SSM_ERR_ALIAS
+    # Unsupported flags and tuning options.
+    assert _scan(lib, opts=bd.ScanOpts(0, 0, 0, 0x80, 0, None)) == bd.SSM_ERR_UNSUPPORTED
+    assert _scan(lib, opts=bd.ScanOpts(3, 0, 0, 0, 0, None)) == bd.SSM_ERR_UNSUPPORTED
+    assert _scan(lib, opts=bd.ScanOpts(16, 0, 0, 0, 0, None)) == bd.SSM_ERR_UNSUPPORTED
+    assert _scan(lib, opts=bd.ScanOpts(0, 0, -5, 0, 0, None)) == bd.SSM_ERR_UNSUPPORTED
+    # A split sequence needs workspace of the queried size, 256-byte aligned.
+    o = bd.ScanOpts(0, 0, 2, 0, 0, None)
+    need = lib.ssm_scan_fwd_ex_workspace_size(2, 4, 8, 16, ctypes.byref(o))
+    assert need == (3 * 2 - 2) * 2 * 8 * 16 * 4
+    assert _scan(lib, opts=o) == bd.SSM_ERR_WORKSPACE
+    assert _scan(lib, opts=o, ws=P0 + 20 * MB, ws_bytes=need - 4) == bd.SSM_ERR_WORKSPACE
+    assert _scan(lib, opts=o, ws=P0 + 20 * MB + 16, ws_bytes=need) == bd.SSM_ERR_MISALIGNED
+    assert _scan(lib, opts=o, ws=P0 + 8 * MB, ws_bytes=need) == bd.SSM_ERR_ALIAS
+
+
+def test_empty_scans_return_before_any_launch(lib):
+    assert _scan(lib, batch=0, x=None, delta=None, y=None, B=None, C=None) == bd.SSM_OK
+    assert _scan(lib, d=0, x=None, delta=None, y=None, A=None) == bd.SSM_OK
+    # seqlen 0 without h_last: nothing to hand over.
+    assert _scan(lib, L=0, x=None, delta=None, y=None, B=None, C=None) == bd.SSM_OK
+
+
+def _upd(lib, h=P0, x=P0 + MB, delta=P0 + 2 * MB, A=P0 + 3 * MB, B=P0 + 4 * MB, C=P0 + 5 * MB, D=None, z=None,
+         y=P0 + 6 * MB, batch=2, d=8, N=16, dtype=1, flags=0):
+    return lib.ssm_state_update_ex(h, x, delta, A, B, C, D, z, y, batch, d, N, dtype, flags, None, None)
+
+
+def test_update_argument_errors(lib):
+    assert _upd(lib, h=None) == bd.SSM_ERR_NULL_ARG
+    assert _upd(lib, C=None) == bd.SSM_ERR_NULL_ARG
+    assert _upd(lib, batch=-2) == bd.SSM_ERR_BAD_DIM
+    assert _upd(lib, N=128) == bd.SSM_ERR_UNSUPPORTED
+    assert _upd(lib, N=6) == bd.SSM_ERR_UNSUPPORTED
+    assert _upd(lib, dtype=2) == bd.SSM_ERR_UNSUPPORTED
+    assert _upd(lib, flags=0x40) == bd.SSM_ERR_UNSUPPORTED
+    assert _upd(lib, h=P0 + 8) == bd.SSM_ERR_MISALIGNED
+    assert _upd(lib, A=P0 + 3 * MB + 4) == bd.SSM_ERR_MISALIGNED
+    assert _upd(lib, x=P0 + MB + 1) == bd.SSM_ERR_MISALIGNED
+    assert _upd(lib, y=P0 + MB) == bd.SSM_ERR_ALIAS
+    assert _upd(lib, h=P0 + 3 * MB) == bd.SSM_ERR_ALIAS
+    assert _upd(lib, batch=0, h=None, x=None, delta=None, y=None) == bd.SSM_OK
+
+
+@pytest.mark.parametrize("shape,expect_split,expect_chunks", [
+    ((2, 64, 32, 16), 8, 1),            # tiny layer: widest split, one chunk
+    ((8, 2048, 1536, 16), 8, 1),        # Mamba-130M layer
+    ((32, 4096, 4096, 16), 1, 1),       # Mamba-1.4B layer: enough channels already
+    ((4, 32768, 5120, 16), 8, 1),       # Mamba-2.8B long layer
+    ((1, 65536, 1024, 16), 8, 16),      # one long sequence: chunked
+])
+def test_launch_plan(lib, shape, expect_split, expect_chunks):
+    g, cl, nc = bd.scan_plan(*shape)
+    assert g == expect_split
+    assert nc == expect_chunks
+    assert cl * nc >= shape[1] > cl * (nc - 1)
+    assert bd.scan_workspace_size(*shape) == (0 if nc == 1 else (3 * nc - 2) * shape[0] * shape[2] * shape[3] * 4)
+
+
+def test_plan_respects_overrides(lib):
+    assert bd.scan_plan(2, 100, 64, 16, n_split=2, chunk_len=7) == (2, 7, 15)
+    assert bd.scan_plan(2, 100, 64, 128)[0] == 8
+    assert bd.scan_plan(2, 100, 64, 2)[0] == 1
+    with pytest.raises(bd.SsmError):
+        bd.scan_plan(2, 100, 64, 16, n_split=16)
