@@ -39,12 +39,24 @@
 #include "ssm_internal.h"
 
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 namespace ssm {
 namespace {
 
 constexpr int kTB = kTimeBlock;
+// Steps ahead of the current block whose B/C lines are warmed into L2.
+constexpr int kFar = 3 * kTB;
+
+// Steps per scalar-load group: keeps the two groups of B/C rows in flight
+// within ~32 SGPRs (bf16 rows are NS/2 dwords each for B and for C), which
+// is kP * NS * 6 ~ 96 VALU slots of cover per group whatever NS is.
+template <typename T, int NS>
+constexpr int row_group() {
+  constexpr int budget = sizeof(T) == 2 ? 16 : 8;
+  return budget / NS < kTB ? (budget / NS > 0 ? budget / NS : 1) : kTB;
+}
 
 struct SweepDims {
   int64_t batch, seqlen, d_inner, chunk_len;
@@ -76,14 +88,15 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
   const int chunk = bid % dm.n_chunks_grid;
   const int64_t b = bid / dm.n_chunks_grid;
 
-  const int64_t DI = dm.d_inner, L = dm.seqlen;
+  const int64_t DI = dm.d_inner;
   const int N = dm.d_state;
   const int64_t d = (int64_t)tile * 64 + lane;
   const bool dvalid = d < DI;
   const int64_t dc = dvalid ? d : DI - 1;  // tail lanes read a valid channel, store nothing
   const int n0 = wv * NS;
+  // Time inside the chunk runs in int32 (the host keeps seqlen below 2^31 - 64).
   const int64_t t_beg = (int64_t)chunk * dm.chunk_len;
-  const int64_t t_end = min(L, t_beg + dm.chunk_len);
+  const int nsteps = (int)(min(dm.seqlen, t_beg + dm.chunk_len) - t_beg);
 
   float Al2[NS], h[NS];
   {
@@ -103,38 +116,60 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
   const float Dv = (!SUMMARY && D != nullptr && wv == 0) ? D[dc] : 0.f;
   const bool has_z = !SUMMARY && z != nullptr;
 
-  // Row pointers are wave-uniform (SGPR); each lane adds its channel offset.
-  const int64_t row0 = b * L;
+  // Wave-uniform pointers (SGPRs) to the chunk's first (b, t) row; each lane
+  // adds its channel offset lc, so loads use the SGPR-base addressing form and
+  // all per-step address arithmetic stays on the scalar unit.
+  const int64_t row0 = b * dm.seqlen + t_beg;
   const int64_t cbase = (int64_t)tile * 64;
   const int lc = (int)(dc - cbase);
   const T* xrow = x + row0 * DI + cbase;
   const T* drow = delta + row0 * DI + cbase;
   const T* zrow = has_z ? z + row0 * DI + cbase : xrow;
+  T* yrow = SUMMARY ? nullptr : y + row0 * DI + cbase;
   const T* Bp = B + row0 * N + n0;
   const T* Cp = C + row0 * N + n0;
 
-  StateRow<T, NS> bn, cn;
-  bn.load(Bp + t_beg * N);
-  if (!SUMMARY) cn.load(Cp + t_beg * N);
+  // B/C rows travel in groups of kP steps through SGPRs: the rows of group
+  // k+1 are requested as soon as group k's rows have landed, so each request
+  // has kP steps of VALU work to arrive in.  (Scalar loads may return out of
+  // order; the only safe wait is for all of them, once per group.)
+  constexpr int kP = row_group<T, NS>();
+  StateRow<T, NS> bq[kP], cq[kP];
+#pragma unroll
+  for (int j = 0; j < kP; ++j) {
+    const int tt = min(j, nsteps - 1);
+    bq[j].load(Bp + (int64_t)tt * N);
+    if (!SUMMARY) cq[j].load(Cp + (int64_t)tt * N);
+  }
 
   T xn[kTB], dn[kTB], zn[kTB];
 #pragma unroll
   for (int i = 0; i < kTB; ++i) zn[i] = T(0);
-  auto fetch = [&](int64_t tb) {
+  auto fetch = [&](int tb) {
 #pragma unroll
     for (int i = 0; i < kTB; ++i) {
-      const int64_t off = min(tb + i, t_end - 1) * DI;
-      xn[i] = xrow[off + lc];
-      dn[i] = drow[off + lc];
-      if (has_z && (i & (g - 1)) == wv) zn[i] = zrow[off + lc];
+      const int64_t off = (int64_t)min(tb + i, nsteps - 1) * DI;
+      const T* xs = xrow + off;
+      const T* ds = drow + off;
+      xn[i] = xs[lc];
+      dn[i] = ds[lc];
+      if (has_z && (i & (g - 1)) == wv) {
+        const T* zs = zrow + off;
+        zn[i] = zs[lc];
+      }
     }
   };
-  fetch(t_beg);
+  fetch(0);
+
+  // L2 warm-up: 16 lanes touch the B and C rows kFar steps ahead with vector
+  // loads (no scalar-counter wait); the value is folded into a sink so the
+  // loads are kept, and consumed a block later when they have long landed.
+  uint32_t pf_sink = 0, pf_last = 0;
 
   float dsum = 0.f;
   int buf = 0;
-  for (int64_t t0 = t_beg; t0 < t_end; t0 += kTB) {
-    const int nt = (int)min((int64_t)kTB, t_end - t0);
+  for (int tb = 0; tb < nsteps; tb += kTB) {
+    const int nt = min(kTB, nsteps - tb);
     T xr[kTB], dr[kTB], zr[kTB];
 #pragma unroll
     for (int i = 0; i < kTB; ++i) {
@@ -142,23 +177,16 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
       dr[i] = dn[i];
       zr[i] = zn[i];
     }
-    if (t0 + kTB < t_end) fetch(t0 + kTB);
+    if (tb + kTB < nsteps) fetch(tb + kTB);
+    pf_sink ^= pf_last;
+    if (lane < 16) {
+      const int tt = min(tb + kFar + (lane & 7), nsteps - 1);
+      const T* src = ((lane & 8) && !SUMMARY) ? Cp + (int64_t)tt * N : Bp + (int64_t)tt * N;
+      pf_last = *reinterpret_cast<const uint32_t*>(src);
+    }
 
     float part[kTB];
-    auto step = [&](int i) {
-      const int64_t t = t0 + i;
-      // Scalar loads return out of order, so consuming this step's B/C row
-      // needs every outstanding scalar load to land.  Touch the row first,
-      // then request the next row, so that request has a whole step of VALU
-      // work to arrive in.
-      const StateRow<T, NS> bc = bn, cc = cn;
-      bc.touch();
-      if (!SUMMARY) cc.touch();
-      __builtin_amdgcn_sched_barrier(0);
-      const int64_t tn = min(t + 1, t_end - 1);
-      bn.load(Bp + tn * N);
-      if (!SUMMARY) cn.load(Cp + tn * N);
-      __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](int i, const StateRow<T, NS>& bc, const StateRow<T, NS>& cc) {
       const float xv = io_to_f32(xr[i]);
       const float dv = io_to_f32(dr[i]);
       const float wx = dv * xv;
@@ -172,24 +200,47 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
       if (SUMMARY) dsum += dv;
       part[i] = acc;
     };
+    auto group = [&](int sb, auto full_t) {
+      constexpr bool kFull = decltype(full_t)::value;
+      bq[0].touch();
+      if (!SUMMARY) cq[0].touch();
+      __builtin_amdgcn_sched_barrier(0);
+      StateRow<T, NS> bc[kP], cc[kP];
+#pragma unroll
+      for (int j = 0; j < kP; ++j) {
+        bc[j] = bq[j];
+        cc[j] = cq[j];
+      }
+#pragma unroll
+      for (int j = 0; j < kP; ++j) {
+        const int tt = min(tb + sb + kP + j, nsteps - 1);
+        bq[j].load(Bp + (int64_t)tt * N);
+        if (!SUMMARY) cq[j].load(Cp + (int64_t)tt * N);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kP; ++j)
+        if (kFull || sb + j < nt) step(sb + j, bc[j], cc[j]);
+    };
     if (nt == kTB) {
 #pragma unroll
-      for (int i = 0; i < kTB; ++i) step(i);
+      for (int sb = 0; sb < kTB; sb += kP) group(sb, std::true_type{});
     } else {
 #pragma unroll
-      for (int i = 0; i < kTB; ++i)
-        if (i < nt) step(i);
+      for (int sb = 0; sb < kTB; sb += kP)
+        if (sb < nt) group(sb, std::false_type{});
     }
 
     if (!SUMMARY) {
-      T* yb = y + (row0 + t0) * DI + cbase;
+      T* yb = yrow + (int64_t)tb * DI;
       if (g == 1) {
 #pragma unroll
         for (int i = 0; i < kTB; ++i) {
           if (i < nt) {
             float v = part[i];
             if (has_z) v *= silu(io_to_f32(zr[i]));
-            if (dvalid) io_store(yb + i * DI + lc, v);
+            T* ys = yb + (int64_t)i * DI;
+            if (dvalid) io_store(ys + lc, v);
           }
         }
       } else {
@@ -204,13 +255,18 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
             float v = 0.f;
             for (int j = 0; j < g; ++j) v += base[(j * kTB + i) * 64];
             if (has_z) v *= silu(io_to_f32(zr[i]));
-            if (dvalid) io_store(yb + i * DI + lc, v);
+            T* ys = yb + (int64_t)i * DI;
+            if (dvalid) io_store(ys + lc, v);
           }
         }
         buf ^= 1;
       }
     }
   }
+  // Let the last scalar and warm-up loads land before the wave ends.
+  bq[0].touch();
+  if (!SUMMARY) cq[0].touch();
+  asm volatile("" ::"v"(pf_sink ^ pf_last));
 
   if (SUMMARY) {
     if (dvalid) {

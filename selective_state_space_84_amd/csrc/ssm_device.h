@@ -37,9 +37,16 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
   return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
+// Read-only view of global memory in the constant address space.  B and C
+// are never written while a kernel runs, and loads through this address space
+// with a wave-uniform address always compile to scalar loads (through a
+// generic pointer the compiler must first prove that no store in the kernel
+// can clobber them, and inside the sweep loop that proof fails).
+typedef const uint32_t __attribute__((address_space(4)))* const_u32_ptr;
+typedef const float __attribute__((address_space(4)))* const_f32_ptr;
+
 // B/C row fragment for one wave: NS consecutive states of one (b, t), held in
-// SGPRs (the address is wave-uniform and the buffers are read-only, so the
-// compiler issues scalar loads).
+// SGPRs and fed to the VALU as scalar operands.
 template <typename T, int NS>
 struct StateRow;
 
@@ -47,8 +54,8 @@ template <int NS>
 struct StateRow<uint16_t, NS> {
   static_assert(NS % 2 == 0, "bf16 rows are loaded as dwords");
   uint32_t w[NS / 2];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ p) {
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    const_u32_ptr q = (const_u32_ptr)(const void*)p;
 #pragma unroll
     for (int k = 0; k < NS / 2; ++k) w[k] = q[k];
   }
@@ -64,9 +71,10 @@ struct StateRow<uint16_t, NS> {
 template <int NS>
 struct StateRow<float, NS> {
   float w[NS];
-  __device__ __forceinline__ void load(const float* __restrict__ p) {
+  __device__ __forceinline__ void load(const float* p) {
+    const_f32_ptr q = (const_f32_ptr)(const void*)p;
 #pragma unroll
-    for (int k = 0; k < NS; ++k) w[k] = p[k];
+    for (int k = 0; k < NS; ++k) w[k] = q[k];
   }
   __device__ __forceinline__ void touch() const { asm volatile("" ::"s"(__builtin_bit_cast(uint32_t, w[0]))); }
   __device__ __forceinline__ float get(int n) const { return w[n]; }
