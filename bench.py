@@ -44,18 +44,20 @@ def _kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(workload: str, source_sha: str, launches: int):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
-    path = os.path.join(REPO, "profiles", "traffic.json")
+def _traffic(workload: str, source_sha: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    the counters were taken on the current kernel sources; else None."""
+    path = os.path.join(REPO, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
-        table = json.load(fh)
-    rec = table.get(workload)
-    if not rec or rec.get("source_sha") != source_sha:
-        return None
-    return rec["bytes_per_launch"]
+        for line in fh:
+            f = line.split()
+            if not f or f[0].startswith("#"):
+                continue
+            if f[0] == workload and f[2] == source_sha:
+                return int(f[7])
+    return None
 
 
 def algorithmic_scan_bytes(batch, seqlen, d_inner, d_state, io_bytes, h0, h_last):
@@ -147,6 +149,7 @@ def bench_decode(steps, dev):
         "achieved_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "frac_of_8tbs": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "input_gen_s": round(gen_s, 1),
+        "traffic_bytes_per_step": _traffic(cfg.name, _kernel_source_sha()),
         "note": "time per step includes launch gaps between 1000 back-to-back eager launches; "
                 "the 84 MB state can stay resident in the 256 MB Infinity Cache between steps",
     }
@@ -228,7 +231,6 @@ def main():
     slots = scan_slots_per_element(cfg.d_state)
     achieved_slots = el_per_s * slots / 1e12
     sha = _kernel_source_sha()
-    launches = 1 if n_chunks == 1 else 3
     out = {
         "metric": "selective-scan elements/s (B·L·d_inner) and achieved HBM GB/s vs peak",
         "value": round(el_per_s, 1),
@@ -249,7 +251,7 @@ def main():
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "alu", "achieved": round(achieved_slots, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                      "unit": "Tslot/s", "frac": round(achieved_slots / VALU_PEAK_TSLOTS, 4),
-                     "traffic": _traffic(cfg.name, sha, launches),
+                     "traffic": _traffic(cfg.name, sha) if n_chunks == 1 else None,
                      "slots_per_element": slots, "kernel": "k_scan_sweep (one launch per step)"},
         "roofline_hbm": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": alg_bytes},

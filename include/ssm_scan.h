@@ -154,7 +154,8 @@ int ssm_scan_fwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_
  *   Alignment      : every pointer aligned to its element size; B and C to 4 bytes.
  *   d_state        : 2, 4, 8, 16, 32, 64 or 128.
  *   Sizes          : batch, seqlen, d_inner >= 0 (any of them 0 is a valid
- *                    empty call; with seqlen 0, h_last receives h0).
+ *                    empty call; with seqlen 0, h_last receives h0);
+ *                    seqlen <= 2^31 - 257 and d_inner <= 2^26, else SSM_ERR_BAD_DIM.
  */
 int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const void* z, const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen,

@@ -57,8 +57,14 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, c
     g = o->n_split;
     if (!is_pow2(g) || g < gmin || g > gmax) return SSM_ERR_UNSUPPORTED;
   } else {
+    // Each extra wave per tile repeats the per-step fixed work (widening,
+    // delta*x, loop and scalar traffic) and adds an LDS exchange: measured
+    // on MI355X, 4 waves per tile cost ~1.4x the VALU work of 1.  So split
+    // the states over at most 2 waves and get further parallelism from
+    // sequence chunks.
+    const int gpref = gmax < 2 ? gmax : (gmin > 2 ? gmin : 2);
     g = gmin;
-    while (g < gmax && base * g < kTargetWaves) g *= 2;
+    while (g < gpref && base * g < kTargetWaves) g *= 2;
   }
   int64_t chunk_len;
   if (o != nullptr && o->chunk_len < 0) return SSM_ERR_UNSUPPORTED;
@@ -67,7 +73,7 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, c
   } else {
     int64_t nch = 1;
     const int64_t waves = base * g;
-    if (waves > 0 && waves * 2 <= kTargetWaves && seqlen >= 2 * kMinAutoChunk) {
+    if (waves > 0 && waves < kTargetWaves && seqlen >= 2 * kMinAutoChunk) {
       nch = (kTargetWaves + waves - 1) / waves;
       if (nch > seqlen / kMinAutoChunk) nch = seqlen / kMinAutoChunk;
     }
@@ -85,8 +91,15 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, c
 bool scan_d_state_ok(int64_t n) { return n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64 || n == 128; }
 bool update_d_state_ok(int64_t n) { return n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64; }
 
+// The sweep counts time inside a chunk in int32 and addresses a block of
+// kTimeBlock rows with 32-bit per-lane byte offsets; these bounds keep both
+// exact (seqlen < 2^31 - 256, kTimeBlock * d_inner * 4 bytes < 2^32).
+constexpr int64_t kMaxSeqlen = INT32_MAX - 256;
+constexpr int64_t kMaxDInner = (int64_t)1 << 26;
+
 int check_dims(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
   if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0) return SSM_ERR_BAD_DIM;
+  if (seqlen > kMaxSeqlen || d_inner > kMaxDInner) return SSM_ERR_BAD_DIM;
   return SSM_OK;
 }
 

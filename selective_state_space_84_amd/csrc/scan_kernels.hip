@@ -60,27 +60,32 @@ constexpr int row_group() {
 
 struct SweepDims {
   int64_t batch, seqlen, d_inner, chunk_len;
-  int32_t d_state, n_split, tiles, n_chunks_grid;  // chunks covered by this launch
-  int32_t n_chunks;                                // chunks of the whole sequence
-  int32_t h_init_chunked;                          // h_init is [n_chunks][B][d][N] (else [B][d][N])
+  int32_t tiles, n_chunks_grid;  // chunks covered by this launch
+  int32_t n_chunks;              // chunks of the whole sequence
+  int32_t h_init_chunked;        // h_init is [n_chunks][B][d][N] (else [B][d][N])
 };
 
-// SUMMARY = true: chunk summary sweep (state from zero, no readout); writes
-// P = exp(A * sum(delta)) and the end state S for chunk c into sumP / sumS.
-// SUMMARY = false: full sweep with readout, gate and y store.
-template <typename T, int NS, bool SUMMARY>
-__global__ void __launch_bounds__(64 * kMaxSplit)
+// One sweep over a (batch row, chunk, 64-channel tile).  N = d_state, NS =
+// states per wave, G = N / NS waves per workgroup.
+// SUMMARY = true: chunk summary (state from zero, no readout): writes
+// P = exp(A * sum(delta)) and the end state S of chunk c into sumP / sumS.
+// SUMMARY = false: full sweep with readout, gate, y store and h_last.
+template <typename T, int N, int NS, bool SUMMARY>
+__global__ void __launch_bounds__(64 * (N / NS))
     k_scan_sweep(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
                  const T* __restrict__ B, const T* __restrict__ C, const float* __restrict__ D,
                  const T* __restrict__ z, const float* __restrict__ h_init, T* __restrict__ y,
                  float* __restrict__ h_last, float* __restrict__ sumP, float* __restrict__ sumS,
                  const SweepDims dm) {
-  extern __shared__ float red[];  // [2][g][kTB][64] partial readouts when g > 1
+  constexpr int G = N / NS;
+  constexpr int kP = row_group<T, NS>();
+  static_assert(G >= 1 && G <= kMaxSplit && NS * G == N, "bad split");
+  static_assert(kTB % kP == 0, "groups tile a block");
+  extern __shared__ float red[];  // [2][G][kTB][64] partial readouts when G > 1
   const int lane = threadIdx.x & 63;
   // Wave index within the workgroup; readfirstlane tells the compiler it is
   // wave-uniform, so everything derived from it stays in SGPRs.
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = dm.n_split;
+  const int wv = G == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = bid % dm.tiles;
@@ -89,7 +94,6 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
   const int64_t b = bid / dm.n_chunks_grid;
 
   const int64_t DI = dm.d_inner;
-  const int N = dm.d_state;
   const int64_t d = (int64_t)tile * 64 + lane;
   const bool dvalid = d < DI;
   const int64_t dc = dvalid ? d : DI - 1;  // tail lanes read a valid channel, store nothing
@@ -116,24 +120,30 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
   const float Dv = (!SUMMARY && D != nullptr && wv == 0) ? D[dc] : 0.f;
   const bool has_z = !SUMMARY && z != nullptr;
 
-  // Wave-uniform pointers (SGPRs) to the chunk's first (b, t) row; each lane
-  // adds its channel offset lc, so loads use the SGPR-base addressing form and
-  // all per-step address arithmetic stays on the scalar unit.
+  // Addressing: x, delta, z and y share one layout, so a block of kTB rows is
+  // reached from one wave-uniform (SGPR) row pointer per tensor plus per-lane
+  // byte offsets voff[i] = (lc + i * d_inner) * sizeof(T), computed once.
+  // Loads and stores then use the SGPR-base form and the per-block pointer
+  // step is the only address arithmetic (scalar) in the steady state.
   const int64_t row0 = b * dm.seqlen + t_beg;
   const int64_t cbase = (int64_t)tile * 64;
   const int lc = (int)(dc - cbase);
-  const T* xrow = x + row0 * DI + cbase;
-  const T* drow = delta + row0 * DI + cbase;
-  const T* zrow = has_z ? z + row0 * DI + cbase : xrow;
-  T* yrow = SUMMARY ? nullptr : y + row0 * DI + cbase;
+  uint32_t voff[kTB];
+#pragma unroll
+  for (int i = 0; i < kTB; ++i) voff[i] = (uint32_t)((lc + (int64_t)i * DI) * (int64_t)sizeof(T));
+  const int64_t blk_bytes = (int64_t)kTB * DI * (int64_t)sizeof(T);
+  const char* xb = reinterpret_cast<const char*>(x + row0 * DI + cbase);
+  const char* db = reinterpret_cast<const char*>(delta + row0 * DI + cbase);
+  const char* zb = has_z ? reinterpret_cast<const char*>(z + row0 * DI + cbase) : xb;
+  char* yb = SUMMARY ? nullptr : reinterpret_cast<char*>(y + row0 * DI + cbase);
   const T* Bp = B + row0 * N + n0;
   const T* Cp = C + row0 * N + n0;
+  auto ld = [](const char* base, uint32_t off) { return *reinterpret_cast<const T*>(base + off); };
 
   // B/C rows travel in groups of kP steps through SGPRs: the rows of group
   // k+1 are requested as soon as group k's rows have landed, so each request
   // has kP steps of VALU work to arrive in.  (Scalar loads may return out of
   // order; the only safe wait is for all of them, once per group.)
-  constexpr int kP = row_group<T, NS>();
   StateRow<T, NS> bq[kP], cq[kP];
 #pragma unroll
   for (int j = 0; j < kP; ++j) {
@@ -141,25 +151,30 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
     bq[j].load(Bp + (int64_t)tt * N);
     if (!SUMMARY) cq[j].load(Cp + (int64_t)tt * N);
   }
+  const T* bnext = Bp + kP * N;  // row of the next group to request
+  const T* cnext = Cp + kP * N;
 
   T xn[kTB], dn[kTB], zn[kTB];
 #pragma unroll
   for (int i = 0; i < kTB; ++i) zn[i] = T(0);
-  auto fetch = [&](int tb) {
+  auto own = [&](int i) { return G == 1 || (i & (G - 1)) == wv; };
+  // Loads of block tb (first row at xb..).  CLAMP: rows past the chunk end
+  // repeat its last row (only the final blocks of a chunk need it).
+  auto fetch = [&](int tb, auto clamp_t) {
+    constexpr bool kClamp = decltype(clamp_t)::value;
 #pragma unroll
     for (int i = 0; i < kTB; ++i) {
-      const int64_t off = (int64_t)min(tb + i, nsteps - 1) * DI;
-      const T* xs = xrow + off;
-      const T* ds = drow + off;
-      xn[i] = xs[lc];
-      dn[i] = ds[lc];
-      if (has_z && (i & (g - 1)) == wv) {
-        const T* zs = zrow + off;
-        zn[i] = zs[lc];
+      uint32_t o = voff[i];
+      if (kClamp) {
+        const int ii = min(tb + i, nsteps - 1) - tb;
+        o = (uint32_t)((lc + (int64_t)ii * DI) * (int64_t)sizeof(T));
       }
+      xn[i] = ld(xb, o);
+      dn[i] = ld(db, o);
+      if (has_z && own(i)) zn[i] = ld(zb, o);
     }
   };
-  fetch(0);
+  fetch(0, std::integral_constant<bool, true>{});
 
   // L2 warm-up: 16 lanes touch the B and C rows kFar steps ahead with vector
   // loads (no scalar-counter wait); the value is folded into a sink so the
@@ -168,8 +183,12 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
 
   float dsum = 0.f;
   int buf = 0;
-  for (int tb = 0; tb < nsteps; tb += kTB) {
-    const int nt = min(kTB, nsteps - tb);
+
+  // One block of kTB steps starting at tb.  FULL: no clamping anywhere
+  // (callers guarantee tb + 2 * kTB <= nsteps).
+  auto block = [&](int tb, auto full_t) {
+    constexpr bool kFull = decltype(full_t)::value;
+    const int nt = kFull ? kTB : min(kTB, nsteps - tb);
     T xr[kTB], dr[kTB], zr[kTB];
 #pragma unroll
     for (int i = 0; i < kTB; ++i) {
@@ -177,7 +196,14 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
       dr[i] = dn[i];
       zr[i] = zn[i];
     }
-    if (tb + kTB < nsteps) fetch(tb + kTB);
+    xb += blk_bytes;
+    db += blk_bytes;
+    zb += blk_bytes;
+    if (kFull) {
+      fetch(tb + kTB, std::integral_constant<bool, false>{});
+    } else if (tb + kTB < nsteps) {
+      fetch(tb + kTB, std::integral_constant<bool, true>{});
+    }
     pf_sink ^= pf_last;
     if (lane < 16) {
       const int tt = min(tb + kFar + (lane & 7), nsteps - 1);
@@ -200,8 +226,9 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
       if (SUMMARY) dsum += dv;
       part[i] = acc;
     };
-    auto group = [&](int sb, auto full_t) {
-      constexpr bool kFull = decltype(full_t)::value;
+#pragma unroll
+    for (int sb = 0; sb < kTB; sb += kP) {
+      if (!kFull && sb >= nt) break;
       bq[0].touch();
       if (!SUMMARY) cq[0].touch();
       __builtin_amdgcn_sched_barrier(0);
@@ -211,58 +238,68 @@ __global__ void __launch_bounds__(64 * kMaxSplit)
         bc[j] = bq[j];
         cc[j] = cq[j];
       }
+      if (kFull) {
 #pragma unroll
-      for (int j = 0; j < kP; ++j) {
-        const int tt = min(tb + sb + kP + j, nsteps - 1);
-        bq[j].load(Bp + (int64_t)tt * N);
-        if (!SUMMARY) cq[j].load(Cp + (int64_t)tt * N);
+        for (int j = 0; j < kP; ++j) {
+          bq[j].load(bnext + j * N);
+          if (!SUMMARY) cq[j].load(cnext + j * N);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kP; ++j) {
+          const int tt = min(tb + sb + kP + j, nsteps - 1);
+          bq[j].load(Bp + (int64_t)tt * N);
+          if (!SUMMARY) cq[j].load(Cp + (int64_t)tt * N);
+        }
       }
+      bnext += kP * N;
+      cnext += kP * N;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < kP; ++j)
         if (kFull || sb + j < nt) step(sb + j, bc[j], cc[j]);
-    };
-    if (nt == kTB) {
-#pragma unroll
-      for (int sb = 0; sb < kTB; sb += kP) group(sb, std::true_type{});
-    } else {
-#pragma unroll
-      for (int sb = 0; sb < kTB; sb += kP)
-        if (sb < nt) group(sb, std::false_type{});
     }
 
     if (!SUMMARY) {
-      T* yb = yrow + (int64_t)tb * DI;
-      if (g == 1) {
+      if (G == 1) {
+        // Whole-block regions (one uniform branch for the gate, one lane mask
+        // for the stores) keep the step arithmetic in the loop body instead
+        // of being sunk into per-step branches.
+        if (has_z) {
 #pragma unroll
-        for (int i = 0; i < kTB; ++i) {
-          if (i < nt) {
-            float v = part[i];
-            if (has_z) v *= silu(io_to_f32(zr[i]));
-            T* ys = yb + (int64_t)i * DI;
-            if (dvalid) io_store(ys + lc, v);
-          }
+          for (int i = 0; i < kTB; ++i) part[i] *= silu(io_to_f32(zr[i]));
+        }
+        if (dvalid) {
+#pragma unroll
+          for (int i = 0; i < kTB; ++i)
+            if (kFull || i < nt) io_store(reinterpret_cast<T*>(yb + voff[i]), part[i]);
         }
       } else {
-        float* mine = red + ((buf * g + wv) * kTB) * 64 + lane;
+        float* mine = red + ((buf * G + wv) * kTB) * 64 + lane;
 #pragma unroll
         for (int i = 0; i < kTB; ++i) mine[i * 64] = part[i];
         __syncthreads();
-        const float* base = red + (buf * g * kTB) * 64 + lane;
+        const float* base = red + (buf * G * kTB) * 64 + lane;
 #pragma unroll
         for (int i = 0; i < kTB; ++i) {
-          if ((i & (g - 1)) == wv && i < nt) {
+          if (own(i) && (kFull || i < nt)) {
             float v = 0.f;
-            for (int j = 0; j < g; ++j) v += base[(j * kTB + i) * 64];
+#pragma unroll
+            for (int j = 0; j < G; ++j) v += base[(j * kTB + i) * 64];
             if (has_z) v *= silu(io_to_f32(zr[i]));
-            T* ys = yb + (int64_t)i * DI;
-            if (dvalid) io_store(ys + lc, v);
+            if (dvalid) io_store(reinterpret_cast<T*>(yb + voff[i]), v);
           }
         }
         buf ^= 1;
       }
+      yb += blk_bytes;
     }
-  }
+  };
+
+  int tb = 0;
+  for (; tb + 2 * kTB <= nsteps; tb += kTB) block(tb, std::true_type{});
+  for (; tb < nsteps; tb += kTB) block(tb, std::false_type{});
+
   // Let the last scalar and warm-up loads land before the wave ends.
   bq[0].touch();
   if (!SUMMARY) cq[0].touch();
@@ -319,13 +356,13 @@ hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem, h
   return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, s);
 }
 
-template <typename T, int NS>
+template <typename T, int N, int NS>
 hipError_t launch_scan_t(const ScanLaunch& p) {
-  const int g = p.n_split;
+  constexpr int G = N / NS;
   const int64_t tiles = (p.d_inner + 63) / 64;
-  const int64_t states = p.batch * p.d_inner * p.d_state;
-  const size_t shmem = g > 1 ? (size_t)2 * g * kTB * 64 * sizeof(float) : 0;
-  SweepDims dm{p.batch, p.seqlen, p.d_inner, p.chunk_len, p.d_state, g, (int32_t)tiles, 1, (int32_t)p.n_chunks, 0};
+  const int64_t states = p.batch * p.d_inner * N;
+  const size_t shmem = G > 1 ? (size_t)2 * G * kTB * 64 * sizeof(float) : 0;
+  SweepDims dm{p.batch, p.seqlen, p.d_inner, p.chunk_len, (int32_t)tiles, 1, (int32_t)p.n_chunks, 0};
   const T* x = static_cast<const T*>(p.x);
   const T* dl = static_cast<const T*>(p.delta);
   const T* Bm = static_cast<const T*>(p.B);
@@ -339,7 +376,7 @@ hipError_t launch_scan_t(const ScanLaunch& p) {
     float* hent = sumS + (p.n_chunks - 1) * states;
     SweepDims ds = dm;
     ds.n_chunks_grid = (int32_t)(p.n_chunks - 1);
-    e = launch(k_scan_sweep<T, NS, true>, dim3((unsigned)(p.batch * (p.n_chunks - 1) * tiles)), dim3(64 * g), 0,
+    e = launch(k_scan_sweep<T, N, NS, true>, dim3((unsigned)(p.batch * (p.n_chunks - 1) * tiles)), dim3(64 * G), 0,
                p.stream, x, dl, p.A, Bm, Cm, p.D, zz, (const float*)nullptr, y, p.h_last, sumP, sumS, ds);
     if (e != hipSuccess) return e;
     e = launch(k_chunk_carry, dim3((unsigned)((states + 255) / 256)), dim3(256), 0, p.stream, p.h0,
@@ -347,29 +384,36 @@ hipError_t launch_scan_t(const ScanLaunch& p) {
     if (e != hipSuccess) return e;
     dm.n_chunks_grid = (int32_t)p.n_chunks;
     dm.h_init_chunked = 1;
-    return launch(k_scan_sweep<T, NS, false>, dim3((unsigned)(p.batch * p.n_chunks * tiles)), dim3(64 * g), shmem,
+    return launch(k_scan_sweep<T, N, NS, false>, dim3((unsigned)(p.batch * p.n_chunks * tiles)), dim3(64 * G), shmem,
                   p.stream, x, dl, p.A, Bm, Cm, p.D, zz, (const float*)hent, y, p.h_last, (float*)nullptr,
                   (float*)nullptr, dm);
   }
-  return launch(k_scan_sweep<T, NS, false>, dim3((unsigned)(p.batch * tiles)), dim3(64 * g), shmem, p.stream, x, dl,
-                p.A, Bm, Cm, p.D, zz, p.h0, y, p.h_last, (float*)nullptr, (float*)nullptr, dm);
+  return launch(k_scan_sweep<T, N, NS, false>, dim3((unsigned)(p.batch * tiles)), dim3(64 * G), shmem, p.stream, x,
+                dl, p.A, Bm, Cm, p.D, zz, p.h0, y, p.h_last, (float*)nullptr, (float*)nullptr, dm);
 }
 
+// Supported (d_state, states per wave) pairs: states per wave in {2,4,8,16},
+// at most 8 waves per tile.
 template <typename T>
-hipError_t launch_scan_ns(const ScanLaunch& p) {
-  switch (p.d_state / p.n_split) {
-    case 2: return launch_scan_t<T, 2>(p);
-    case 4: return launch_scan_t<T, 4>(p);
-    case 8: return launch_scan_t<T, 8>(p);
-    case 16: return launch_scan_t<T, 16>(p);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_scan_n(const ScanLaunch& p) {
+  const int ns = p.d_state / p.n_split;
+#define SSM_CASE(N_, NS_) \
+  if (p.d_state == N_ && ns == NS_) return launch_scan_t<T, N_, NS_>(p);
+  SSM_CASE(2, 2)
+  SSM_CASE(4, 4) SSM_CASE(4, 2)
+  SSM_CASE(8, 8) SSM_CASE(8, 4) SSM_CASE(8, 2)
+  SSM_CASE(16, 16) SSM_CASE(16, 8) SSM_CASE(16, 4) SSM_CASE(16, 2)
+  SSM_CASE(32, 16) SSM_CASE(32, 8) SSM_CASE(32, 4)
+  SSM_CASE(64, 16) SSM_CASE(64, 8)
+  SSM_CASE(128, 16)
+#undef SSM_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_scan(const ScanLaunch& p) {
-  return p.bf16 ? launch_scan_ns<uint16_t>(p) : launch_scan_ns<float>(p);
+  return p.bf16 ? launch_scan_n<uint16_t>(p) : launch_scan_n<float>(p);
 }
 
 hipError_t launch_state_fill(float* dst, const float* src, int64_t states, hipStream_t stream) {

@@ -60,8 +60,9 @@ struct StateRow<uint16_t, NS> {
     for (int k = 0; k < NS / 2; ++k) w[k] = q[k];
   }
   // Marks the row as consumed here (an empty asm reading an SGPR), which
-  // makes the compiler wait for its scalar load at this point.
-  __device__ __forceinline__ void touch() const { asm volatile("" ::"s"(w[0])); }
+  // makes the compiler wait for its scalar load at this point.  The memory
+  // clobber keeps later row loads from being hoisted above it.
+  __device__ __forceinline__ void touch() const { asm volatile("" ::"s"(w[0]) : "memory"); }
   __device__ __forceinline__ float get(int n) const {
     const uint32_t v = w[n >> 1];
     return __builtin_bit_cast(float, (n & 1) ? (v & 0xffff0000u) : (v << 16));
@@ -76,7 +77,9 @@ struct StateRow<float, NS> {
 #pragma unroll
     for (int k = 0; k < NS; ++k) w[k] = q[k];
   }
-  __device__ __forceinline__ void touch() const { asm volatile("" ::"s"(__builtin_bit_cast(uint32_t, w[0]))); }
+  __device__ __forceinline__ void touch() const {
+    asm volatile("" ::"s"(__builtin_bit_cast(uint32_t, w[0])) : "memory");
+  }
   __device__ __forceinline__ float get(int n) const { return w[n]; }
 };
 

@@ -54,6 +54,8 @@ def test_scan_argument_errors(lib):
     assert _scan(lib, N=256) == bd.SSM_ERR_UNSUPPORTED
     assert _scan(lib, dtype=7) == bd.SSM_ERR_UNSUPPORTED
     assert _scan(lib, batch=1 << 40, L=1 << 20, d=1 << 10) == bd.SSM_ERR_BAD_DIM
+    assert _scan(lib, batch=1, L=(1 << 31) - 100, d=1) == bd.SSM_ERR_BAD_DIM
+    assert _scan(lib, batch=1, L=1, d=(1 << 26) + 1) == bd.SSM_ERR_BAD_DIM
     assert _scan(lib, x=P0 + 1) == bd.SSM_ERR_MISALIGNED
     assert _scan(lib, dtype=0, delta=P0 + MB + 2) == bd.SSM_ERR_MISALIGNED
     assert _scan(lib, B=P0 + 3 * MB + 2) == bd.SSM_ERR_MISALIGNED
@@ -106,11 +108,12 @@ def test_update_argument_errors(lib):
 
 
 @pytest.mark.parametrize("shape,expect_split,expect_chunks", [
-    ((2, 64, 32, 16), 8, 1),            # tiny layer: widest split, one chunk
-    ((8, 2048, 1536, 16), 8, 1),        # Mamba-130M layer
+    ((2, 64, 32, 16), 2, 1),            # tiny layer: too short to chunk
+    ((8, 2048, 1536, 16), 2, 4),        # Mamba-130M layer: 2 waves per tile, 4 chunks
     ((32, 4096, 4096, 16), 1, 1),       # Mamba-1.4B layer: enough channels already
-    ((4, 32768, 5120, 16), 8, 1),       # Mamba-2.8B long layer
-    ((1, 65536, 1024, 16), 8, 16),      # one long sequence: chunked
+    ((4, 32768, 5120, 16), 2, 4),       # Mamba-2.8B long layer
+    ((1, 65536, 1024, 16), 2, 64),      # one long sequence: many chunks
+    ((2, 4096, 256, 128), 8, 8),        # d_state 128 needs 8 waves per tile
 ])
 def test_launch_plan(lib, shape, expect_split, expect_chunks):
     g, cl, nc = bd.scan_plan(*shape)
