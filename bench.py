@@ -38,7 +38,7 @@ def scan_slots_per_element(d_state: int) -> int:
 
 def _kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("scan_kernels.hip", "update_kernel.hip", "ssm_device.h", "ssm_internal.h"):
+    for f in ("scan_sweep.h", "scan_mode0.hip", "scan_aux.hip", "update_kernel.hip", "ssm_device.h", "ssm_internal.h"):
         with open(os.path.join(REPO, "selective_state_space_84_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

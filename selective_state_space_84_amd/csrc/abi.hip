@@ -21,6 +21,7 @@ constexpr int64_t kTargetWaves = 2048;
 constexpr int64_t kMinAutoChunk = 512;
 // Workspace alignment the library asks for.
 constexpr uintptr_t kWorkspaceAlign = 256;
+constexpr uint32_t kKnownFlags = SSM_FLAG_DELTA_SOFTPLUS | SSM_FLAG_EXACT_ZOH;
 
 bool mul3(int64_t a, int64_t b, int64_t c, int64_t* out) {
   int64_t t;
@@ -127,7 +128,9 @@ int scan_impl(const void* x, const void* delta, const float* A, const void* B, c
   if (rc != SSM_OK) return rc;
   if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
   if (!scan_d_state_ok(d_state)) return SSM_ERR_UNSUPPORTED;
-  if (opts != nullptr && opts->flags != 0) return SSM_ERR_UNSUPPORTED;
+  const uint32_t flags = opts != nullptr ? opts->flags : 0u;
+  const float* dt_bias = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? opts->dt_bias : nullptr;
+  if (flags & ~kKnownFlags) return SSM_ERR_UNSUPPORTED;
   const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
 
   int64_t n_io, n_bc, n_h, n_a;
@@ -144,10 +147,12 @@ int scan_impl(const void* x, const void* delta, const float* A, const void* B, c
   if (n_io > 0 && (x == nullptr || delta == nullptr || y == nullptr)) return SSM_ERR_NULL_ARG;
   if (n_bc > 0 && n_io > 0 && (B == nullptr || C == nullptr)) return SSM_ERR_NULL_ARG;
   if (n_a > 0 && n_io > 0 && A == nullptr) return SSM_ERR_NULL_ARG;
+  if ((flags & SSM_FLAG_DELTA_SOFTPLUS) && d_inner > 0 && dt_bias == nullptr) return SSM_ERR_NULL_ARG;
 
   // Alignment.
   if (!aligned(x, es) || !aligned(delta, es) || !aligned(z, es) || !aligned(y, es)) return SSM_ERR_MISALIGNED;
-  if (!aligned(B, 4) || !aligned(C, 4) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) || !aligned(h_last, 4))
+  if (!aligned(B, 4) || !aligned(C, 4) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) || !aligned(h_last, 4) ||
+      !aligned(dt_bias, 4))
     return SSM_ERR_MISALIGNED;
 
   // Aliasing: y overlaps nothing; h_last overlaps nothing except h0 exactly.
@@ -156,6 +161,8 @@ int scan_impl(const void* x, const void* delta, const float* A, const void* B, c
   for (int k = 0; k < 8; ++k)
     if (overlap(y, b_io, ins[k], inb[k])) return SSM_ERR_ALIAS;
   if (overlap(y, b_io, h_last, h_last ? b_h : 0)) return SSM_ERR_ALIAS;
+  if (overlap(y, b_io, dt_bias, dt_bias ? b_d : 0) || overlap(h_last, h_last ? b_h : 0, dt_bias, dt_bias ? b_d : 0))
+    return SSM_ERR_ALIAS;
   if (h_last != nullptr) {
     for (int k = 0; k < 7; ++k)
       if (overlap(h_last, b_h, ins[k], inb[k])) return SSM_ERR_ALIAS;
@@ -174,10 +181,10 @@ int scan_impl(const void* x, const void* delta, const float* A, const void* B, c
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return SSM_ERR_WORKSPACE;
     if (!aligned(workspace, kWorkspaceAlign)) return SSM_ERR_MISALIGNED;
-    const void* all[] = {x, delta, z, B, C, A, D, h0, y, h_last};
+    const void* all[] = {x, delta, z, B, C, A, D, h0, y, h_last, dt_bias};
     const int64_t allb[] = {b_io, b_io, z ? b_io : 0, b_bc, b_bc, b_a, D ? b_d : 0, h0 ? b_h : 0, b_io,
-                            h_last ? b_h : 0};
-    for (int k = 0; k < 10; ++k)
+                            h_last ? b_h : 0, dt_bias ? b_d : 0};
+    for (int k = 0; k < 11; ++k)
       if (overlap(workspace, (int64_t)need, all[k], allb[k])) return SSM_ERR_ALIAS;
   }
   int64_t state_blocks = (n_h + 255) / 256;
@@ -189,19 +196,20 @@ int scan_impl(const void* x, const void* delta, const float* A, const void* B, c
     if (h_last == nullptr || h_last == h0) return SSM_OK;
     return ssm::launch_state_fill(h_last, h0, n_h, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
-  ssm::ScanLaunch p{x, delta, A, B, C, D, z, h0, y, h_last, static_cast<float*>(workspace), batch, seqlen, d_inner,
-                    (int32_t)d_state, pl.n_split, pl.chunk_len, pl.n_chunks, io_dtype == SSM_DTYPE_BF16, s};
+  ssm::ScanLaunch p{x, delta, A, B, C, D, z, h0, y, h_last, static_cast<float*>(workspace), dt_bias, flags, batch,
+                    seqlen, d_inner, (int32_t)d_state, pl.n_split, pl.chunk_len, pl.n_chunks,
+                    io_dtype == SSM_DTYPE_BF16, s};
   return ssm::launch_scan(p) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 int update_impl(float* h, const void* x_t, const void* delta_t, const float* A, const void* B_t, const void* C_t,
                 const float* D, const void* z_t, void* y_t, int64_t batch, int64_t d_inner, int64_t d_state,
                 int32_t io_dtype, uint32_t flags, const float* dt_bias, void* stream) {
-  (void)dt_bias;
   if (batch < 0 || d_inner < 0 || d_state <= 0) return SSM_ERR_BAD_DIM;
   if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
   if (!update_d_state_ok(d_state)) return SSM_ERR_UNSUPPORTED;
-  if (flags != 0) return SSM_ERR_UNSUPPORTED;
+  if (flags & ~kKnownFlags) return SSM_ERR_UNSUPPORTED;
+  if (!(flags & SSM_FLAG_DELTA_SOFTPLUS)) dt_bias = nullptr;
   const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
   int64_t n_io, n_h, n_bc;
   if (!mul3(batch, d_inner, 1, &n_io) || !mul3(batch, d_inner, d_state, &n_h) || !mul3(batch, d_state, 1, &n_bc))
@@ -213,6 +221,8 @@ int update_impl(float* h, const void* x_t, const void* delta_t, const float* A, 
   if (n_io > 0 && (h == nullptr || x_t == nullptr || delta_t == nullptr || y_t == nullptr || A == nullptr ||
                    B_t == nullptr || C_t == nullptr))
     return SSM_ERR_NULL_ARG;
+  if ((flags & SSM_FLAG_DELTA_SOFTPLUS) && n_io > 0 && dt_bias == nullptr) return SSM_ERR_NULL_ARG;
+  if (!aligned(dt_bias, 4)) return SSM_ERR_MISALIGNED;
   const uintptr_t ha = d_state >= 4 ? 16 : 8;
   if (!aligned(h, ha) || !aligned(A, ha)) return SSM_ERR_MISALIGNED;
   if (!aligned(x_t, es) || !aligned(delta_t, es) || !aligned(z_t, es) || !aligned(y_t, es)) return SSM_ERR_MISALIGNED;
@@ -226,9 +236,11 @@ int update_impl(float* h, const void* x_t, const void* delta_t, const float* A, 
     if (overlap(h, b_h, ins[k], inb[k])) return SSM_ERR_ALIAS;
   }
   if (overlap(h, b_h, y_t, b_io)) return SSM_ERR_ALIAS;
+  if (overlap(y_t, b_io, dt_bias, dt_bias ? d_inner * 4 : 0) || overlap(h, b_h, dt_bias, dt_bias ? d_inner * 4 : 0))
+    return SSM_ERR_ALIAS;
   if (ssm::update_grid_blocks(batch, d_inner, (int32_t)d_state) > INT32_MAX) return SSM_ERR_BAD_DIM;
   if (n_io == 0) return SSM_OK;
-  ssm::UpdateLaunch p{h, x_t, delta_t, A, B_t, C_t, D, z_t, y_t, batch, d_inner, (int32_t)d_state,
+  ssm::UpdateLaunch p{h, x_t, delta_t, A, B_t, C_t, D, z_t, y_t, dt_bias, flags, batch, d_inner, (int32_t)d_state,
                       io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream)};
   return ssm::launch_update(p) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

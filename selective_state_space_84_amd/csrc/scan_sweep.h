@@ -1,4 +1,5 @@
-// Selective-scan kernels for gfx950 (MI355X).
+// Selective-scan sweep kernel for gfx950 (MI355X), shared by the per-mode
+// translation units scan_mode{0,1,2,3}.hip.
 //
 // What is computed (per batch row b, channel d, state n; A diagonal):
 //   abar = exp(delta[b,t,d] * A[d,n])                     -- decay
@@ -35,15 +36,27 @@
 //     runs each chunk from its true entry state.
 //   * Workgroup ids are remapped so each XCD gets a contiguous range of
 //     (batch row, chunk, tile), keeping a row's B/C lines in one L2.
+//
+// Modes (compile-time bits, so the default path carries no extra work):
+//   kSoftplusDelta: the step is softplus(delta + dt_bias[d]) (selection step,
+//     derivation page section 4.1), computed in-kernel from the raw projection.
+//   kExactZoh: the input term is the exact zero-order hold
+//     (exp(delta a) - 1) / a * B (derivation page section 2.2; "Mamba from
+//     principle to code" section 2.2) instead of delta * B; a = 0 takes the
+//     limit delta * B.  The coefficient comes from zoh_coef (ssm_device.h),
+//     accurate to ~5e-7 relative, including where delta * a is tiny.
+#pragma once
+
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
-#include <tuple>
 #include <type_traits>
-#include <utility>
 
 namespace ssm {
 namespace {
+
+constexpr int kSoftplusDelta = 1;
+constexpr int kExactZoh = 2;
 
 constexpr int kTB = kTimeBlock;
 // Steps ahead of the current block whose B/C lines are warmed into L2.
@@ -51,10 +64,13 @@ constexpr int kFar = 3 * kTB;
 
 // Steps per scalar-load group: keeps the two groups of B/C rows in flight
 // within ~32 SGPRs (bf16 rows are NS/2 dwords each for B and for C), which
-// is kP * NS * 6 ~ 96 VALU slots of cover per group whatever NS is.
+// is kP * NS * 6 ~ 96 VALU slots of cover per group whatever NS is.  A wave
+// that owns all 16 states has the fewest other scalar values live and takes
+// two-step groups (measured ~5% faster on MI355X; for smaller NS the larger
+// groups spill).
 template <typename T, int NS>
 constexpr int row_group() {
-  constexpr int budget = sizeof(T) == 2 ? 16 : 8;
+  constexpr int budget = sizeof(T) == 2 ? (NS == 16 ? 32 : 16) : 8;
   return budget / NS < kTB ? (budget / NS > 0 ? budget / NS : 1) : kTB;
 }
 
@@ -70,13 +86,13 @@ struct SweepDims {
 // SUMMARY = true: chunk summary (state from zero, no readout): writes
 // P = exp(A * sum(delta)) and the end state S of chunk c into sumP / sumS.
 // SUMMARY = false: full sweep with readout, gate, y store and h_last.
-template <typename T, int N, int NS, bool SUMMARY>
+template <typename T, int N, int NS, bool SUMMARY, int MODE>
 __global__ void __launch_bounds__(64 * (N / NS))
     k_scan_sweep(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
                  const T* __restrict__ B, const T* __restrict__ C, const float* __restrict__ D,
                  const T* __restrict__ z, const float* __restrict__ h_init, T* __restrict__ y,
                  float* __restrict__ h_last, float* __restrict__ sumP, float* __restrict__ sumS,
-                 const SweepDims dm) {
+                 const float* __restrict__ dt_bias, const SweepDims dm) {
   constexpr int G = N / NS;
   constexpr int kP = row_group<T, NS>();
   static_assert(G >= 1 && G <= kMaxSplit && NS * G == N, "bad split");
@@ -103,11 +119,17 @@ __global__ void __launch_bounds__(64 * (N / NS))
   const int nsteps = (int)(min(dm.seqlen, t_beg + dm.chunk_len) - t_beg);
 
   float Al2[NS], h[NS];
+  float ia[(MODE & kExactZoh) ? NS : 1];  // 1/a for the exact-ZOH coefficient
   {
     const float* Ap = A + dc * N + n0;
 #pragma unroll
-    for (int n = 0; n < NS; ++n) Al2[n] = Ap[n] * kLog2e;
+    for (int n = 0; n < NS; ++n) {
+      const float a = Ap[n];
+      Al2[n] = a * kLog2e;
+      if (MODE & kExactZoh) ia[n] = 1.0f / a;
+    }
   }
+  const float dtb = (MODE & kSoftplusDelta) ? dt_bias[dc] : 0.f;
   if (!SUMMARY && h_init != nullptr) {
     const int64_t row = dm.h_init_chunked ? ((int64_t)chunk * dm.batch + b) * DI + dc : b * DI + dc;
     const float* hp = h_init + row * N + n0;
@@ -214,13 +236,20 @@ __global__ void __launch_bounds__(64 * (N / NS))
     float part[kTB];
     auto step = [&](int i, const StateRow<T, NS>& bc, const StateRow<T, NS>& cc) {
       const float xv = io_to_f32(xr[i]);
-      const float dv = io_to_f32(dr[i]);
+      float dv = io_to_f32(dr[i]);
+      if (MODE & kSoftplusDelta) dv = softplus(dv + dtb);
       const float wx = dv * xv;
       float acc = Dv * xv;
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
-        const float ab = hw_exp2(dv * Al2[n]);
-        h[n] = __builtin_fmaf(ab, h[n], wx * bc.get(n));
+        const float yv = dv * Al2[n];
+        const float ab = hw_exp2(yv);
+        if (MODE & kExactZoh) {
+          const float coef = zoh_coef(yv, ab, dv, ia[n]);
+          h[n] = __builtin_fmaf(coef, xv * bc.get(n), ab * h[n]);
+        } else {
+          h[n] = __builtin_fmaf(ab, h[n], wx * bc.get(n));
+        }
         if (!SUMMARY) acc = __builtin_fmaf(cc.get(n), h[n], acc);
       }
       if (SUMMARY) dsum += dv;
@@ -321,42 +350,7 @@ __global__ void __launch_bounds__(64 * (N / NS))
   }
 }
 
-// Entry state of every chunk: H[0] = h0, H[c+1] = P[c] * H[c] + S[c].
-// One lane per (b, d, n) state; lanes are contiguous in memory, so every
-// access is coalesced.  The chunk loop is the associative combine applied in
-// order (the pairs are few, so a tree would only add work).
-__global__ void __launch_bounds__(256) k_chunk_carry(const float* __restrict__ h0, const float* __restrict__ sumP,
-                                                     const float* __restrict__ sumS, float* __restrict__ h_entry,
-                                                     int64_t states, int64_t n_chunks) {
-  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (s >= states) return;
-  float hc = h0 != nullptr ? h0[s] : 0.f;
-  h_entry[s] = hc;
-  for (int64_t c = 0; c + 1 < n_chunks; ++c) {
-    hc = __builtin_fmaf(sumP[c * states + s], hc, sumS[c * states + s]);
-    h_entry[(c + 1) * states + s] = hc;
-  }
-}
-
-// h_last for an empty sequence: the state is handed over unchanged.
-__global__ void __launch_bounds__(256) k_state_fill(float* __restrict__ dst, const float* __restrict__ src,
-                                                    int64_t states) {
-  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (s < states) dst[s] = src != nullptr ? src[s] : 0.f;
-}
-
-template <typename... KArgs, typename... Args>
-hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t s, Args&&... args) {
-  std::tuple<KArgs...> vals(std::forward<Args>(args)...);
-  void* ptrs[sizeof...(KArgs)];
-  std::apply([&](auto&... v) {
-    int k = 0;
-    ((ptrs[k++] = static_cast<void*>(&v)), ...);
-  }, vals);
-  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, s);
-}
-
-template <typename T, int N, int NS>
+template <typename T, int N, int NS, int MODE>
 hipError_t launch_scan_t(const ScanLaunch& p) {
   constexpr int G = N / NS;
   const int64_t tiles = (p.d_inner + 63) / 64;
@@ -376,29 +370,28 @@ hipError_t launch_scan_t(const ScanLaunch& p) {
     float* hent = sumS + (p.n_chunks - 1) * states;
     SweepDims ds = dm;
     ds.n_chunks_grid = (int32_t)(p.n_chunks - 1);
-    e = launch(k_scan_sweep<T, N, NS, true>, dim3((unsigned)(p.batch * (p.n_chunks - 1) * tiles)), dim3(64 * G), 0,
-               p.stream, x, dl, p.A, Bm, Cm, p.D, zz, (const float*)nullptr, y, p.h_last, sumP, sumS, ds);
+    e = launch(k_scan_sweep<T, N, NS, true, MODE>, dim3((unsigned)(p.batch * (p.n_chunks - 1) * tiles)), dim3(64 * G), 0,
+               p.stream, x, dl, p.A, Bm, Cm, p.D, zz, (const float*)nullptr, y, p.h_last, sumP, sumS, p.dt_bias, ds);
     if (e != hipSuccess) return e;
-    e = launch(k_chunk_carry, dim3((unsigned)((states + 255) / 256)), dim3(256), 0, p.stream, p.h0,
-               (const float*)sumP, (const float*)sumS, hent, states, p.n_chunks);
+    e = launch_chunk_carry(p.h0, sumP, sumS, hent, states, p.n_chunks, p.stream);
     if (e != hipSuccess) return e;
     dm.n_chunks_grid = (int32_t)p.n_chunks;
     dm.h_init_chunked = 1;
-    return launch(k_scan_sweep<T, N, NS, false>, dim3((unsigned)(p.batch * p.n_chunks * tiles)), dim3(64 * G), shmem,
+    return launch(k_scan_sweep<T, N, NS, false, MODE>, dim3((unsigned)(p.batch * p.n_chunks * tiles)), dim3(64 * G), shmem,
                   p.stream, x, dl, p.A, Bm, Cm, p.D, zz, (const float*)hent, y, p.h_last, (float*)nullptr,
-                  (float*)nullptr, dm);
+                  (float*)nullptr, p.dt_bias, dm);
   }
-  return launch(k_scan_sweep<T, N, NS, false>, dim3((unsigned)(p.batch * tiles)), dim3(64 * G), shmem, p.stream, x,
-                dl, p.A, Bm, Cm, p.D, zz, p.h0, y, p.h_last, (float*)nullptr, (float*)nullptr, dm);
+  return launch(k_scan_sweep<T, N, NS, false, MODE>, dim3((unsigned)(p.batch * tiles)), dim3(64 * G), shmem, p.stream, x,
+                dl, p.A, Bm, Cm, p.D, zz, p.h0, y, p.h_last, (float*)nullptr, (float*)nullptr, p.dt_bias, dm);
 }
 
 // Supported (d_state, states per wave) pairs: states per wave in {2,4,8,16},
 // at most 8 waves per tile.
-template <typename T>
+template <typename T, int MODE>
 hipError_t launch_scan_n(const ScanLaunch& p) {
   const int ns = p.d_state / p.n_split;
 #define SSM_CASE(N_, NS_) \
-  if (p.d_state == N_ && ns == NS_) return launch_scan_t<T, N_, NS_>(p);
+  if (p.d_state == N_ && ns == NS_) return launch_scan_t<T, N_, NS_, MODE>(p);
   SSM_CASE(2, 2)
   SSM_CASE(4, 4) SSM_CASE(4, 2)
   SSM_CASE(8, 8) SSM_CASE(8, 4) SSM_CASE(8, 2)
@@ -410,14 +403,10 @@ hipError_t launch_scan_n(const ScanLaunch& p) {
   return hipErrorInvalidValue;
 }
 
+template <int MODE>
+hipError_t launch_scan_for_mode(const ScanLaunch& p) {
+  return p.bf16 ? launch_scan_n<uint16_t, MODE>(p) : launch_scan_n<float, MODE>(p);
+}
+
 }  // namespace
-
-hipError_t launch_scan(const ScanLaunch& p) {
-  return p.bf16 ? launch_scan_n<uint16_t>(p) : launch_scan_n<float>(p);
-}
-
-hipError_t launch_state_fill(float* dst, const float* src, int64_t states, hipStream_t stream) {
-  return launch(k_state_fill, dim3((unsigned)((states + 255) / 256)), dim3(256), 0, stream, dst, src, states);
-}
-
 }  // namespace ssm

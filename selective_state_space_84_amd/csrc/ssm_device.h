@@ -7,6 +7,7 @@
 namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // bf16 is carried as its raw 16-bit pattern.  Widening to fp32 puts the 16
 // bits in the top half of the word (exact).
@@ -21,10 +22,50 @@ __device__ __forceinline__ void io_store(float* p, float v) { *p = v; }
 // fix-up; results below the normal range flush towards zero).
 __device__ __forceinline__ float hw_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 __device__ __forceinline__ float hw_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+__device__ __forceinline__ float hw_log2(float v) { return __builtin_amdgcn_logf(v); }
+
+// softplus(v) = log(1 + e^v).
+//  * e^v = 2^(v log2 e): the rounding of the product v * log2(e) (|v| up to
+//    ~10 here) would cost ~5e-7 relative in e^v, so the product is split into
+//    hi + lo (one FMA, plus log2(e)'s own low part) and e^v is corrected to
+//    first order in lo.
+//  * With u = 1 + e^v rounded, log(u) loses the low bits of a small e^v; the
+//    factor e^v / (u - 1) restores them (Kahan's log1p rearrangement).
+// For v > 20 the result is v to fp32 precision (and e^v may overflow).
+constexpr float kLog2eLo = 1.925963e-8f;  // log2(e) - (float)log2(e)
+__device__ __forceinline__ float softplus(float v) {
+  const float yh = v * kLog2e;
+  const float yl = __builtin_fmaf(v, kLog2e, -yh) + v * kLog2eLo;
+  float e = hw_exp2(yh);
+  e = __builtin_fmaf(e, yl * kLn2, e);
+  const float u = 1.0f + e;
+  const float um1 = u - 1.0f;
+  const float r = um1 == 0.0f ? e : hw_log2(u) * kLn2 * (e * hw_rcp(um1));
+  return v > 20.0f ? v : r;
+}
 
 // v * sigmoid(v) = v / (1 + exp(-v)).  For v -> -inf the exponential
 // overflows to +inf and the result is -0; NaN propagates.
 __device__ __forceinline__ float silu(float v) { return v * hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
+
+// Coefficient of B*x in the exact zero-order hold, (exp(delta a) - 1) / a,
+// from y = delta * a * log2(e), abar = 2^y and inv_a = 1/a:
+//   |y| < 1/4: delta * phi, phi = (e^v - 1)/v = sum_k v^k/(k+1)! with v = y ln 2,
+//              to 4th order (truncation < 3e-7 relative); this also covers a = 0;
+//   otherwise: (abar - 1) * inv_a, where abar's rounding is small against
+//              abar - 1 (|abar - 1| > 0.16).
+// Relative error below ~5e-7 over the whole range.
+constexpr float kZoh1 = 0.3465736f;    // ln2 / 2!
+constexpr float kZoh2 = 0.0800755f;    // ln2^2 / 3!
+constexpr float kZoh3 = 0.013876027f;  // ln2^3 / 4!
+constexpr float kZoh4 = 0.0019236258f; // ln2^4 / 5!
+__device__ __forceinline__ float zoh_coef(float y, float abar, float delta, float inv_a) {
+  const float phi =
+      __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(__builtin_fmaf(y, kZoh4, kZoh3), y, kZoh2), y, kZoh1), y, 1.0f);
+  const float small = delta * phi;
+  const float big = __builtin_fmaf(abar, inv_a, -inv_a);
+  return __builtin_fabsf(y) < 0.25f ? small : big;
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X
 // (workgroup i runs on XCD i % 8).  Remap so that each XCD receives one

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace ssm {
 
 // Timesteps per block of the scan sweep (prefetch and readout granularity).
@@ -25,6 +28,8 @@ struct ScanLaunch {
   void* y;
   float* h_last;       // nullable
   float* workspace;    // nullable when n_chunks == 1
+  const float* dt_bias;  // [d_inner], used with SSM_FLAG_DELTA_SOFTPLUS
+  uint32_t flags;        // SSM_FLAG_* (bit 0 softplus step, bit 1 exact ZOH)
   int64_t batch, seqlen, d_inner;
   int32_t d_state;
   int32_t n_split;     // waves per 64-channel tile (1, 2, 4, 8)
@@ -44,6 +49,8 @@ struct UpdateLaunch {
   const float* D;  // nullable
   const void* z;   // nullable
   void* y;
+  const float* dt_bias;  // [d_inner], used with SSM_FLAG_DELTA_SOFTPLUS
+  uint32_t flags;
   int64_t batch, d_inner;
   int32_t d_state;
   bool bf16;
@@ -59,7 +66,26 @@ inline int64_t scan_workspace_floats(int64_t n_chunks, int64_t states) {
 }
 
 hipError_t launch_scan(const ScanLaunch& p);
+template <int MODE>
+hipError_t launch_scan_mode(const ScanLaunch& p);  // one translation unit per MODE
+hipError_t launch_chunk_carry(const float* h0, const float* sumP, const float* sumS, float* h_entry, int64_t states,
+                              int64_t n_chunks, hipStream_t stream);
 hipError_t launch_state_fill(float* dst, const float* src, int64_t states, hipStream_t stream);
 hipError_t launch_update(const UpdateLaunch& p);
+
+// Launches kern with hipLaunchKernel, which reports this launch's own error
+// (the sticky last-error state is left alone).  Arguments are converted to
+// the kernel's parameter types first.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                         Args&&... args) {
+  std::tuple<KArgs...> vals(std::forward<Args>(args)...);
+  void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+  std::apply([&](auto&... v) {
+    int k = 0;
+    ((ptrs[k++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, s);
+}
 
 }  // namespace ssm

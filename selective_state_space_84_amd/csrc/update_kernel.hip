@@ -22,8 +22,6 @@
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
-#include <tuple>
-#include <utility>
 
 namespace ssm {
 namespace {
@@ -88,12 +86,15 @@ __device__ __forceinline__ void load_row(const float* p, float (&v)[SPL]) {
   for (int k = 0; k < SPL; ++k) v[k] = tmp[k];
 }
 
-template <typename T, int SPL, int LPC>
+// MODE bit 0: the step is softplus(delta + dt_bias[d]); bit 1: exact
+// zero-order-hold input term (exp(delta a) - 1) / a * B (limit delta * B at
+// a = 0), as in the scan sweep.
+template <typename T, int SPL, int LPC, int MODE>
 __global__ void __launch_bounds__(kUpdBlock)
     k_state_update(float* __restrict__ h, const T* __restrict__ x, const T* __restrict__ delta,
                    const float* __restrict__ A, const T* __restrict__ B, const T* __restrict__ C,
-                   const float* __restrict__ D, const T* __restrict__ z, T* __restrict__ y, int64_t d_inner,
-                   int32_t blocks_per_row) {
+                   const float* __restrict__ D, const T* __restrict__ z, T* __restrict__ y,
+                   const float* __restrict__ dt_bias, int64_t d_inner, int32_t blocks_per_row) {
   constexpr int N = SPL * LPC;
   constexpr int kChan = kUpdBlock / LPC;  // channels per workgroup
   const int64_t b = blockIdx.x / blocks_per_row;
@@ -112,13 +113,20 @@ __global__ void __launch_bounds__(kUpdBlock)
   load_row<SPL>(C + b * N + s0, Cv);
   const int64_t io = b * d_inner + dc;
   const float xv = io_to_f32(x[io]);
-  const float dv = io_to_f32(delta[io]);
+  float dv = io_to_f32(delta[io]);
+  if (MODE & 1) dv = softplus(dv + dt_bias[dc]);
   const float wx = dv * xv;
   float acc = 0.f;
 #pragma unroll
   for (int n = 0; n < SPL; ++n) {
-    const float ab = hw_exp2(dv * (al[n] * kLog2e));
-    hv[n] = __builtin_fmaf(ab, hv[n], wx * Bv[n]);
+    const float yv = dv * (al[n] * kLog2e);
+    const float ab = hw_exp2(yv);
+    if (MODE & 2) {
+      const float coef = zoh_coef(yv, ab, dv, 1.0f / al[n]);
+      hv[n] = __builtin_fmaf(coef, xv * Bv[n], ab * hv[n]);
+    } else {
+      hv[n] = __builtin_fmaf(ab, hv[n], wx * Bv[n]);
+    }
     acc = __builtin_fmaf(Cv[n], hv[n], acc);
   }
   acc = group_sum<LPC>(acc);
@@ -133,25 +141,24 @@ __global__ void __launch_bounds__(kUpdBlock)
   }
 }
 
-template <typename... KArgs, typename... Args>
-hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t s, Args&&... args) {
-  std::tuple<KArgs...> vals(std::forward<Args>(args)...);
-  void* ptrs[sizeof...(KArgs)];
-  std::apply([&](auto&... v) {
-    int k = 0;
-    ((ptrs[k++] = static_cast<void*>(&v)), ...);
-  }, vals);
-  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, s);
+template <typename T, int SPL, int LPC, int MODE>
+hipError_t launch_update_m(const UpdateLaunch& p) {
+  constexpr int kChan = kUpdBlock / LPC;
+  const int64_t per_row = (p.d_inner + kChan - 1) / kChan;
+  return launch(k_state_update<T, SPL, LPC, MODE>, dim3((unsigned)(p.batch * per_row)), dim3(kUpdBlock), 0, p.stream,
+                p.h, static_cast<const T*>(p.x), static_cast<const T*>(p.delta), p.A, static_cast<const T*>(p.B),
+                static_cast<const T*>(p.C), p.D, static_cast<const T*>(p.z), static_cast<T*>(p.y), p.dt_bias,
+                p.d_inner, (int32_t)per_row);
 }
 
 template <typename T, int SPL, int LPC>
 hipError_t launch_update_t(const UpdateLaunch& p) {
-  constexpr int kChan = kUpdBlock / LPC;
-  const int64_t per_row = (p.d_inner + kChan - 1) / kChan;
-  return launch(k_state_update<T, SPL, LPC>, dim3((unsigned)(p.batch * per_row)), dim3(kUpdBlock), 0, p.stream, p.h,
-                static_cast<const T*>(p.x), static_cast<const T*>(p.delta), p.A, static_cast<const T*>(p.B),
-                static_cast<const T*>(p.C), p.D, static_cast<const T*>(p.z), static_cast<T*>(p.y), p.d_inner,
-                (int32_t)per_row);
+  switch (p.flags & 3u) {
+    case 0: return launch_update_m<T, SPL, LPC, 0>(p);
+    case 1: return launch_update_m<T, SPL, LPC, 1>(p);
+    case 2: return launch_update_m<T, SPL, LPC, 2>(p);
+    default: return launch_update_m<T, SPL, LPC, 3>(p);
+  }
 }
 
 template <typename T>

@@ -66,6 +66,11 @@ def test_scan_argument_errors(lib):
     assert _scan(lib, h0=P0 + 9 * MB, h_last=P0 + 9 * MB + 64) == bd.SSM_ERR_ALIAS
     # Unsupported flags and tuning options.
     assert _scan(lib, opts=bd.ScanOpts(0, 0, 0, 0x80, 0, None)) == bd.SSM_ERR_UNSUPPORTED
+    # The softplus step needs dt_bias: present, 4-byte aligned, not overlapping outputs.
+    sp = bd.SSM_FLAG_DELTA_SOFTPLUS
+    assert _scan(lib, opts=bd.ScanOpts(0, 0, 0, sp, 0, None)) == bd.SSM_ERR_NULL_ARG
+    assert _scan(lib, opts=bd.ScanOpts(0, 0, 0, sp, 0, P0 + 30 * MB + 2)) == bd.SSM_ERR_MISALIGNED
+    assert _scan(lib, opts=bd.ScanOpts(0, 0, 0, sp, 0, P0 + 8 * MB + 4)) == bd.SSM_ERR_ALIAS
     assert _scan(lib, opts=bd.ScanOpts(3, 0, 0, 0, 0, None)) == bd.SSM_ERR_UNSUPPORTED
     assert _scan(lib, opts=bd.ScanOpts(16, 0, 0, 0, 0, None)) == bd.SSM_ERR_UNSUPPORTED
     assert _scan(lib, opts=bd.ScanOpts(0, 0, -5, 0, 0, None)) == bd.SSM_ERR_UNSUPPORTED
@@ -99,6 +104,7 @@ def test_update_argument_errors(lib):
     assert _upd(lib, N=6) == bd.SSM_ERR_UNSUPPORTED
     assert _upd(lib, dtype=2) == bd.SSM_ERR_UNSUPPORTED
     assert _upd(lib, flags=0x40) == bd.SSM_ERR_UNSUPPORTED
+    assert _upd(lib, flags=bd.SSM_FLAG_DELTA_SOFTPLUS) == bd.SSM_ERR_NULL_ARG
     assert _upd(lib, h=P0 + 8) == bd.SSM_ERR_MISALIGNED
     assert _upd(lib, A=P0 + 3 * MB + 4) == bd.SSM_ERR_MISALIGNED
     assert _upd(lib, x=P0 + MB + 1) == bd.SSM_ERR_MISALIGNED
