@@ -57,6 +57,8 @@ def _load():
     lib.ssm_oracle_scan_f64.restype = ctypes.c_int
     lib.ssm_oracle_update_f64.argtypes = [P] * 10 + [I64] * 3 + [ctypes.c_int, ctypes.c_int]
     lib.ssm_oracle_update_f64.restype = ctypes.c_int
+    lib.ssm_oracle_conv1d_f64.argtypes = [P] * 6 + [I64] * 4 + [ctypes.c_int]
+    lib.ssm_oracle_conv1d_f64.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -149,3 +151,30 @@ def scan_channels(inputs, channels, *, exact_zoh=False, delta_softplus=False):
         ys[k] = y[0, :, 0]
         hs[k] = h[0, 0]
     return ys, hs
+
+
+def conv1d(x, w, bias=None, state_in=None, *, silu=True):
+    """Causal depthwise conv over time (+ SiLU).  x: (batch, seqlen, d_inner);
+    w: (d_inner, d_conv); bias: (d_inner,); state_in: (batch, d_inner, d_conv-1).
+    Returns (y, state_out) in fp64."""
+    lib = _load()
+    x, w, bias, state_in = (to_f64(v) for v in (x, w, bias, state_in))
+    batch, seqlen, d_inner = x.shape
+    d_conv = w.shape[1]
+    assert w.shape == (d_inner, d_conv)
+    assert bias is None or bias.shape == (d_inner,)
+    assert state_in is None or state_in.shape == (batch, d_inner, d_conv - 1)
+    y = np.empty_like(x)
+    state_out = np.empty((batch, d_inner, d_conv - 1), dtype=np.float64)
+    rc = lib.ssm_oracle_conv1d_f64(_ptr(x), _ptr(w), _ptr(bias), _ptr(state_in), _ptr(y), _ptr(state_out),
+                                   batch, seqlen, d_inner, d_conv, 1 if silu else 0)
+    if rc != 0:
+        raise ValueError("oracle conv1d rejected its arguments (%d)" % rc)
+    return y, state_out
+
+
+def conv1d_update(state, x_t, w, bias=None, *, silu=True):
+    """One decode step of the conv: state (batch, d_inner, d_conv-1) is NOT
+    modified; returns (y_t, new_state).  x_t: (batch, d_inner)."""
+    y, st = conv1d(np.asarray(to_f64(x_t))[:, None, :], w, bias, state, silu=silu)
+    return y[:, 0, :], st

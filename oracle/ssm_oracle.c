@@ -160,4 +160,50 @@ int ssm_oracle_update_f64(double* h, const double* x_t, const double* delta_t, c
                              input_mode, delta_mode);
 }
 
-int ssm_oracle_version(void) { return 1; }
+/*
+ * Causal depthwise convolution over time, one filter per channel, followed
+ * by an optional SiLU.  "Deriving and implementing Mamba from scratch"
+ * (dpshk.com/news/3333417), section 5.2: Conv1d(d_inner, d_inner,
+ * kernel_size=d_conv, padding=d_conv-1, groups=d_inner, bias=True), output
+ * cut to the first seqlen positions, then SiLU.  With that padding the
+ * output at t sees inputs t-(K-1) .. t, weight k multiplying input
+ * t-(K-1)+k:
+ *     out[t] = bias + sum_{k=0}^{K-1} w[k] * xe[t + k]
+ * where xe is the input extended on the left by K-1 values: the carried
+ * conv state (state_in) if given, else zeros.  The carried state is the
+ * last K-1 entries of xe after the sequence ("SSM series #12" page,
+ * section 1.3: the decode cache holds a convolution state next to the SSM
+ * state).
+ *   x, y      : [batch][seqlen][d_inner]
+ *   w         : [d_inner][d_conv]
+ *   bias      : [d_inner] (nullable: 0)
+ *   state_in  : [batch][d_inner][d_conv-1] (nullable: zeros)
+ *   state_out : [batch][d_inner][d_conv-1] (nullable)
+ */
+int ssm_oracle_conv1d_f64(const double* x, const double* w, const double* bias, const double* state_in, double* y,
+                          double* state_out, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_conv,
+                          int apply_silu) {
+  if (!x || !w || !y) return ORACLE_BAD_ARG;
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_conv < 1) return ORACLE_BAD_ARG;
+  const int64_t K = d_conv, S = d_conv - 1;
+  double* xe = (double*)malloc((size_t)(seqlen + S + 1) * sizeof(double));
+  if (!xe) return ORACLE_BAD_ARG;
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < d_inner; ++d) {
+      for (int64_t j = 0; j < S; ++j) xe[j] = state_in ? state_in[(b * d_inner + d) * S + j] : 0.0;
+      for (int64_t t = 0; t < seqlen; ++t) xe[S + t] = x[(b * seqlen + t) * d_inner + d];
+      for (int64_t t = 0; t < seqlen; ++t) {
+        double acc = bias ? bias[d] : 0.0;
+        for (int64_t k = 0; k < K; ++k) acc += w[d * K + k] * xe[t + k];
+        if (apply_silu) acc = acc / (1.0 + exp(-acc));
+        y[(b * seqlen + t) * d_inner + d] = acc;
+      }
+      if (state_out)
+        for (int64_t j = 0; j < S; ++j) state_out[(b * d_inner + d) * S + j] = xe[seqlen + j];
+    }
+  }
+  free(xe);
+  return ORACLE_OK;
+}
+
+int ssm_oracle_version(void) { return 2; }
