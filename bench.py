@@ -159,6 +159,37 @@ def bench_decode(steps, dev):
     }
 
 
+def bench_conv(cfg, steps, dev, d_conv=4):
+    """Causal depthwise conv1d + SiLU on the scan workload's (batch, seqlen,
+    d_inner): the Mamba block step that produces the scan's x."""
+    import torch
+    from selective_state_space_84_amd import binding, inputs
+    t0 = time.time()
+    inp = inputs.make_conv_inputs(cfg.batch, cfg.seqlen, cfg.d_inner, d_conv, cfg.dtype, 100 + cfg.seed)
+    gen_s = time.time() - t0
+    x, w, b = (to_dev(inp[k], dev) for k in ("x", "w", "bias"))
+    y = torch.empty_like(x)
+    st = torch.empty((cfg.batch, cfg.d_inner, d_conv - 1), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        binding.ssm_conv1d_fwd(x, w, b, y=y, state_out=st)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        binding.ssm_conv1d_fwd(x, w, b, y=y, state_out=st)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    el = cfg.batch * cfg.seqlen * cfg.d_inner
+    io = 2 if cfg.dtype == "bf16" else 4
+    alg = 2 * el * io + cfg.d_inner * (d_conv + 1) * 4 + cfg.batch * cfg.d_inner * (d_conv - 1) * 4
+    return {"workload": cfg.name + " conv1d+silu (d_conv %d)" % d_conv, "steps": steps, "ms_per_step": round(ms, 6),
+            "elements_per_s": round(el / (ms * 1e-3), 1), "algorithmic_bytes_per_step": alg,
+            "achieved_gbps": round(alg / (ms * 1e-3) / 1e9, 1),
+            "frac_of_8tbs": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "input_gen_s": round(gen_s, 1)}
+
+
 def cpu_baseline(cfg, inp, y_dev, hl_dev, budget_s=12.0, flags=0):
     """fp64 oracle (single thread) on whole batch rows of the same workload,
     row after row until the time budget is spent; also compares those rows'
@@ -211,6 +242,7 @@ def main():
     ap.add_argument("--workload", default="mamba-1.4b-layer")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--n-split", type=int, default=0, help="override the launch plan (tuning)")
     ap.add_argument("--chunk-len", type=int, default=0, help="override the launch plan (tuning)")
@@ -275,6 +307,9 @@ def main():
         out["parity"] = par
     del y, hl
     torch.cuda.empty_cache()
+    if not args.no_conv:
+        out["conv1d"] = bench_conv(cfg, args.steps, dev)
+        torch.cuda.empty_cache()
     if not args.no_decode:
         out["decode"] = bench_decode(args.decode_steps, dev)
     print(json.dumps(out), flush=True)

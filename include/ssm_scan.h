@@ -191,6 +191,40 @@ int ssm_state_update_ex(float* h, const void* x_t, const void* delta_t, const fl
                         const void* C_t, const float* D, const void* z_t, void* y_t, int64_t batch, int64_t d_inner,
                         int64_t d_state, int32_t io_dtype, uint32_t flags, const float* dt_bias, void* stream);
 
+/*
+ * Causal depthwise conv1d over time, optionally followed by SiLU: the step
+ * of the Mamba block that produces the scan's x ("Deriving and implementing
+ * Mamba from scratch" (dpshk.com/news/3333417), section 5.2:
+ * Conv1d(d_inner, d_inner, kernel_size=d_conv, padding=d_conv-1,
+ * groups=d_inner, bias=True), output cut to the first seqlen positions, then
+ * SiLU).  With xe = [state_in (d_conv-1 inputs) | x]:
+ *
+ *   y[b,t,d] = act(bias[d] + sum_{k<d_conv} w[d,k] * xe[b, t+k, d])
+ *
+ *   x, y      : [batch][seqlen][d_inner] io_dtype (y must not overlap inputs)
+ *   w         : [d_inner][d_conv] fp32 (PyTorch's (d_inner, 1, d_conv) weight)
+ *   bias      : [d_inner] fp32, or NULL for 0
+ *   state_in  : [batch][d_inner][d_conv-1] fp32 carried inputs, or NULL for zeros
+ *   state_out : [batch][d_inner][d_conv-1] fp32, receives the last d_conv-1
+ *               entries of xe (the decode cache's conv state, "SSM series #12"
+ *               (dpshk.com/news/5205047) section 1.3), or NULL; it may be the
+ *               state_in buffer.
+ *   d_conv    : 2, 3 or 4.  apply_silu: 0 or 1.
+ * Same conventions, validation and error codes as the scan.
+ */
+int ssm_conv1d_fwd(const void* x, const float* w, const float* bias, const float* state_in, void* y,
+                   float* state_out, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_conv,
+                   int32_t io_dtype, int32_t apply_silu, void* stream);
+
+/*
+ * One decode step of the conv: window = [state | x_t], y_t = act(bias + w .
+ * window), state <- window without its oldest entry (in place).
+ *   state : [batch][d_inner][d_conv-1] fp32 (in/out); x_t, y_t: [batch][d_inner].
+ * Equivalent to ssm_conv1d_fwd with seqlen = 1, state_in = state_out = state.
+ */
+int ssm_conv1d_update(float* state, const void* x_t, const float* w, const float* bias, void* y_t, int64_t batch,
+                      int64_t d_inner, int64_t d_conv, int32_t io_dtype, int32_t apply_silu, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,8 @@ SIGNATURES = {
     "ssm_scan_fwd_ex": ([_P] * 10 + [_I64] * 4 + [_I32, ctypes.POINTER(ScanOpts), _P, _SZ, _P], ctypes.c_int),
     "ssm_state_update": ([_P] * 9 + [_I64] * 3 + [_I32, _P], ctypes.c_int),
     "ssm_state_update_ex": ([_P] * 9 + [_I64] * 3 + [_I32, _U32, _P, _P], ctypes.c_int),
+    "ssm_conv1d_fwd": ([_P] * 6 + [_I64] * 4 + [_I32, _I32, _P], ctypes.c_int),
+    "ssm_conv1d_update": ([_P] * 5 + [_I64] * 3 + [_I32, _I32, _P], ctypes.c_int),
 }
 
 _lib = None
@@ -188,4 +190,40 @@ def ssm_state_update(h, x_t, delta_t, A, B_t, C_t, D=None, z_t=None, *, y_t=None
         batch, d_inner, d_state, dt, flags, _ptr(dt_bias), _stream(stream))
     if rc != SSM_OK:
         raise SsmError(rc, "ssm_state_update")
+    return y_t
+
+
+def ssm_conv1d_fwd(x, w, bias=None, state_in=None, *, y=None, state_out=None, want_state=True, silu=True,
+                   stream=None):
+    """Causal depthwise conv1d (+ SiLU); returns (y, state_out).
+
+    x: (batch, seqlen, d_inner) bf16/fp32; w: (d_inner, d_conv) fp32;
+    bias: (d_inner,) fp32; state_in / state_out: (batch, d_inner, d_conv-1) fp32.
+    """
+    import torch
+    batch, seqlen, d_inner = x.shape
+    d_conv = w.shape[1]
+    if y is None:
+        y = torch.empty_like(x)
+    if state_out is None and want_state:
+        state_out = torch.empty((batch, d_inner, d_conv - 1), dtype=torch.float32, device=x.device)
+    rc = load_library().ssm_conv1d_fwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(state_in), _ptr(y), _ptr(state_out),
+                                       batch, seqlen, d_inner, d_conv, _io_dtype(x), 1 if silu else 0,
+                                       _stream(stream))
+    if rc != SSM_OK:
+        raise SsmError(rc, "ssm_conv1d_fwd")
+    return y, state_out
+
+
+def ssm_conv1d_update(state, x_t, w, bias=None, *, y_t=None, silu=True, stream=None):
+    """One decode step of the conv, in place on state (batch, d_inner, d_conv-1); returns y_t."""
+    import torch
+    batch, d_inner = x_t.shape
+    d_conv = w.shape[1]
+    if y_t is None:
+        y_t = torch.empty_like(x_t)
+    rc = load_library().ssm_conv1d_update(_ptr(state), _ptr(x_t), _ptr(w), _ptr(bias), _ptr(y_t), batch, d_inner,
+                                          d_conv, _io_dtype(x_t), 1 if silu else 0, _stream(stream))
+    if rc != SSM_OK:
+        raise SsmError(rc, "ssm_conv1d_update")
     return y_t

@@ -245,9 +245,63 @@ int update_impl(float* h, const void* x_t, const void* delta_t, const float* A, 
   return ssm::launch_update(p) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+int conv_impl(const void* x, const float* w, const float* bias, const float* state_in, void* y, float* state_out,
+              int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_conv, int32_t io_dtype, int32_t apply_silu,
+              void* stream, bool update) {
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_conv <= 0) return SSM_ERR_BAD_DIM;
+  if (seqlen > kMaxSeqlen || d_inner > kMaxDInner) return SSM_ERR_BAD_DIM;
+  if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
+  if (d_conv < 2 || d_conv > 4) return SSM_ERR_UNSUPPORTED;
+  if (apply_silu != 0 && apply_silu != 1) return SSM_ERR_UNSUPPORTED;
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  int64_t n_io, n_st;
+  if (!mul3(batch, update ? 1 : seqlen, d_inner, &n_io) || !mul3(batch, d_inner, d_conv - 1, &n_st))
+    return SSM_ERR_BAD_DIM;
+  int64_t b_io, b_st;
+  if (__builtin_mul_overflow(n_io, es, &b_io) || __builtin_mul_overflow(n_st, (int64_t)4, &b_st))
+    return SSM_ERR_BAD_DIM;
+  const int64_t b_w = d_inner * d_conv * 4, b_b = d_inner * 4;
+  if (n_io > 0 && (x == nullptr || y == nullptr || w == nullptr)) return SSM_ERR_NULL_ARG;
+  if (update && n_st > 0 && state_out == nullptr) return SSM_ERR_NULL_ARG;
+  if (!aligned(x, es) || !aligned(y, es) || !aligned(w, 4) || !aligned(bias, 4) || !aligned(state_in, 4) ||
+      !aligned(state_out, 4))
+    return SSM_ERR_MISALIGNED;
+  const void* ins[] = {x, w, bias, state_in};
+  const int64_t inb[] = {b_io, b_w, bias ? b_b : 0, state_in ? b_st : 0};
+  for (int k = 0; k < 4; ++k)
+    if (overlap(y, b_io, ins[k], inb[k])) return SSM_ERR_ALIAS;
+  if (state_out != nullptr) {
+    for (int k = 0; k < 3; ++k)
+      if (overlap(state_out, b_st, ins[k], inb[k])) return SSM_ERR_ALIAS;
+    if (overlap(state_out, b_st, y, b_io)) return SSM_ERR_ALIAS;
+    if (state_in != nullptr && state_in != state_out && overlap(state_out, b_st, state_in, b_st)) return SSM_ERR_ALIAS;
+  }
+  const int64_t blocks = update ? (batch * d_inner + 255) / 256 : ssm::conv_grid_blocks(batch, seqlen, d_inner);
+  if (blocks > INT32_MAX || (batch * d_inner + 255) / 256 > INT32_MAX) return SSM_ERR_BAD_DIM;
+  if (batch == 0 || d_inner == 0) return SSM_OK;
+  ssm::ConvLaunch p{x, w, bias, state_in, y, state_out, batch, seqlen, d_inner, (int32_t)d_conv, apply_silu == 1,
+                    io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream)};
+  if (update) return ssm::launch_conv1d_update(p) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  if (seqlen == 0 && state_out == nullptr) return SSM_OK;
+  return ssm::launch_conv1d(p) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+int ssm_conv1d_fwd(const void* x, const float* w, const float* bias, const float* state_in, void* y,
+                   float* state_out, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_conv,
+                   int32_t io_dtype, int32_t apply_silu, void* stream) {
+  return conv_impl(x, w, bias, state_in, y, state_out, batch, seqlen, d_inner, d_conv, io_dtype, apply_silu, stream,
+                   false);
+}
+
+int ssm_conv1d_update(float* state, const void* x_t, const float* w, const float* bias, void* y_t, int64_t batch,
+                      int64_t d_inner, int64_t d_conv, int32_t io_dtype, int32_t apply_silu, void* stream) {
+  return conv_impl(x_t, w, bias, nullptr, y_t, state, batch, 1, d_inner, d_conv, io_dtype, apply_silu, stream, true);
+}
+
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 

@@ -57,6 +57,22 @@ struct UpdateLaunch {
   hipStream_t stream;
 };
 
+// One causal conv1d launch (or decode step: x = x_t, y = y_t, state_out = the
+// in-place state, seqlen unused).
+struct ConvLaunch {
+  const void* x;
+  const float* w;         // [d_inner][d_conv]
+  const float* bias;      // nullable
+  const float* state_in;  // nullable
+  void* y;
+  float* state_out;       // nullable (sweep); the state (decode step)
+  int64_t batch, seqlen, d_inner;
+  int32_t d_conv;
+  bool silu;
+  bool bf16;
+  hipStream_t stream;
+};
+
 // Workspace layout used when n_chunks > 1, in floats, with S = batch*d_inner*d_state:
 //   [0, (n_chunks-1)*S)             chunk decay products  P[c][b][d][n]
 //   [(n_chunks-1)*S, 2(n_chunks-1)*S) chunk end states from zero  S[c][b][d][n]
@@ -72,6 +88,9 @@ hipError_t launch_chunk_carry(const float* h0, const float* sumP, const float* s
                               int64_t n_chunks, hipStream_t stream);
 hipError_t launch_state_fill(float* dst, const float* src, int64_t states, hipStream_t stream);
 hipError_t launch_update(const UpdateLaunch& p);
+hipError_t launch_conv1d(const ConvLaunch& p);
+hipError_t launch_conv1d_update(const ConvLaunch& p);
+int64_t conv_grid_blocks(int64_t batch, int64_t seqlen, int64_t d_inner);
 
 // Launches kern with hipLaunchKernel, which reports this launch's own error
 // (the sticky last-error state is left alone).  Arguments are converted to

@@ -221,3 +221,39 @@ def make_decode_inputs(batch: int, d_inner: int, d_state: int, dtype: str, steps
 
 def decode_inputs(cfg: DecodeConfig, steps: Optional[int] = None, threads: Optional[int] = None):
     return make_decode_inputs(cfg.batch, cfg.d_inner, cfg.d_state, cfg.dtype, steps or cfg.steps, cfg.seed, threads)
+
+
+def make_conv_inputs(batch: int, seqlen: int, d_inner: int, d_conv: int, dtype: str, seed: int,
+                     with_state: bool = False, threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Host tensors for the causal conv: x (batch, seqlen, d_inner) ~ N(0,1) in
+    the io type; w (d_inner, d_conv) and bias (d_inner,) ~ U(-1/sqrt(d_conv),
+    1/sqrt(d_conv)) fp32 (the default initialisation of a depthwise Conv1d,
+    fan-in d_conv); state (batch, d_inner, d_conv-1) ~ N(0,1) fp32 or None.
+    SeedSequence(seed).spawn(4) gives [w, bias, x, state]; x is drawn per
+    (batch row, 4096-step segment) like the scan inputs."""
+    kw, kb, kx, ks = np.random.SeedSequence(seed).spawn(4)
+    bound = 1.0 / np.sqrt(d_conv)
+    out = {"w": round_to_f32(np.random.default_rng(kw).uniform(-bound, bound, (d_inner, d_conv))),
+           "bias": round_to_f32(np.random.default_rng(kb).uniform(-bound, bound, d_inner))}
+    nseg = max(1, -(-seqlen // SEGMENT))
+    io_t = np.uint16 if dtype == "bf16" else np.float32
+    x = np.empty((batch, seqlen, d_inner), dtype=io_t)
+    grand = kx.spawn(batch * nseg)
+
+    def fill(task: int):
+        b, s = divmod(task, nseg)
+        t0, t1 = s * SEGMENT, min(seqlen, (s + 1) * SEGMENT)
+        if t1 > t0:
+            x[b, t0:t1] = _to_io(np.random.default_rng(grand[task]).standard_normal((t1 - t0, d_inner)), dtype)
+
+    tasks = batch * nseg
+    if tasks > 1 and batch * seqlen * d_inner > (1 << 20):
+        with ThreadPoolExecutor(_threads(threads)) as ex:
+            list(ex.map(fill, range(tasks)))
+    else:
+        for t in range(tasks):
+            fill(t)
+    out["x"] = x
+    out["state"] = (round_to_f32(np.random.default_rng(ks).standard_normal((batch, d_inner, d_conv - 1)))
+                    if with_state else None)
+    return out

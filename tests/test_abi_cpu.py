@@ -135,3 +135,27 @@ def test_plan_respects_overrides(lib):
     assert bd.scan_plan(2, 100, 64, 2)[0] == 1
     with pytest.raises(bd.SsmError):
         bd.scan_plan(2, 100, 64, 16, n_split=16)
+
+
+def _conv(lib, x=P0, w=P0 + MB, bias=None, st_in=None, y=P0 + 2 * MB, st_out=None, batch=2, L=10, d=8, K=4,
+          dtype=1, silu=1):
+    return lib.ssm_conv1d_fwd(x, w, bias, st_in, y, st_out, batch, L, d, K, dtype, silu, None)
+
+
+def test_conv_argument_errors(lib):
+    assert _conv(lib, x=None) == bd.SSM_ERR_NULL_ARG
+    assert _conv(lib, w=None) == bd.SSM_ERR_NULL_ARG
+    assert _conv(lib, L=-1) == bd.SSM_ERR_BAD_DIM
+    assert _conv(lib, K=1) == bd.SSM_ERR_UNSUPPORTED
+    assert _conv(lib, K=5) == bd.SSM_ERR_UNSUPPORTED
+    assert _conv(lib, silu=2) == bd.SSM_ERR_UNSUPPORTED
+    assert _conv(lib, dtype=3) == bd.SSM_ERR_UNSUPPORTED
+    assert _conv(lib, x=P0 + 1) == bd.SSM_ERR_MISALIGNED
+    assert _conv(lib, st_in=P0 + 3 * MB + 2) == bd.SSM_ERR_MISALIGNED
+    assert _conv(lib, y=P0 + 8) == bd.SSM_ERR_ALIAS
+    assert _conv(lib, st_out=P0 + MB) == bd.SSM_ERR_ALIAS
+    assert _conv(lib, st_in=P0 + 3 * MB, st_out=P0 + 3 * MB + 4) == bd.SSM_ERR_ALIAS
+    assert _conv(lib, batch=0, x=None, y=None) == bd.SSM_OK
+    assert lib.ssm_conv1d_update(None, P0, P0 + MB, None, P0 + 2 * MB, 2, 8, 4, 1, 1, None) == bd.SSM_ERR_NULL_ARG
+    assert lib.ssm_conv1d_update(P0 + 3 * MB, P0, P0 + MB, None, P0 + 2 * MB, 2, 8, 7, 1, 1, None) == \
+        bd.SSM_ERR_UNSUPPORTED
