@@ -42,6 +42,21 @@ def test_decode_steps_full_compare(lib, dtype, d_state):
     assert floored_rel_err(h, hr) <= tol
 
 
+@pytest.mark.parametrize("batch", [1, 2, 7])
+def test_decode_batch_rows(lib, batch):
+    """Every batch count a thread's row pairing can meet: one row, an even count,
+    an odd count whose last pair has no second row."""
+    steps = 4
+    inp = inputs.make_decode_inputs(batch, 200, 16, "f32", steps, 870 + batch)
+    Y, h = _run_steps(inp, steps)
+    hr = np.zeros((batch, 200, 16))
+    for s in range(steps):
+        yr, hr = oracle.update(hr, inp["x"][s], inp["delta"][s], inp["A"], inp["B"][s], inp["C"][s], inp["D"],
+                               inp["z"][s])
+        assert floored_rel_err(Y[s], yr) <= 1e-5, "step %d" % s
+    assert floored_rel_err(h, hr) <= 1e-5
+
+
 def test_decode_without_gate_and_skip(lib):
     steps = 6
     inp = inputs.make_decode_inputs(3, 128, 16, "f32", steps, 850)
