@@ -14,7 +14,10 @@ oracle sees precisely the values the device sees.
 
 Pins: every function here is checked against closed forms, a textbook IIR
 filter, a library ZOH discretisation and brute-force unrolled sums by the
-CPU tests (``tests/test_oracle_pins.py``).
+CPU tests (``tests/test_oracle_pins.py``, ``tests/test_oracle_conv_pins.py``);
+the gradient ``scan_bwd`` against central finite differences of ``scan``,
+Euler identities of the parts of the scan that are linear, and hand-derived
+one-step derivatives (``tests/test_oracle_bwd_pins.py``).
 """
 from __future__ import annotations
 
@@ -59,6 +62,8 @@ def _load():
     lib.ssm_oracle_update_f64.restype = ctypes.c_int
     lib.ssm_oracle_conv1d_f64.argtypes = [P] * 6 + [I64] * 4 + [ctypes.c_int]
     lib.ssm_oracle_conv1d_f64.restype = ctypes.c_int
+    lib.ssm_oracle_scan_bwd_f64.argtypes = [P] * 20 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
+    lib.ssm_oracle_scan_bwd_f64.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -127,6 +132,42 @@ def update(h, x_t, delta_t, A, B_t, C_t, D=None, z_t=None, dt_bias=None, *, exac
     if rc != 0:
         raise ValueError("oracle update rejected its arguments (%d)" % rc)
     return y_t, hn
+
+
+def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dt_bias=None, *, dy, dh_last=None, exact_zoh=False,
+             delta_softplus=False):
+    """Gradient of L = sum(dy * y) + sum(dh_last * h_last) for the scan above.
+
+    Returns a dict of fp64 arrays: dx, ddelta (w.r.t. the delta input as
+    given, i.e. the raw value when delta_softplus), dA, dB, dC, dh0, and dD,
+    dz, d_dt_bias when D, z, delta_softplus are used.
+    """
+    lib = _load()
+    x, delta, A, B, C = (to_f64(v) for v in (x, delta, A, B, C))
+    D, z, h0, dt_bias = (to_f64(v) for v in (D, z, h0, dt_bias))
+    dy, dh_last = to_f64(dy), to_f64(dh_last)
+    batch, seqlen, d_inner = x.shape
+    d_state = A.shape[1]
+    assert delta.shape == x.shape and dy.shape == x.shape and A.shape == (d_inner, d_state)
+    assert B.shape == (batch, seqlen, d_state) and C.shape == B.shape
+    assert dh_last is None or dh_last.shape == (batch, d_inner, d_state)
+    assert h0 is None or h0.shape == (batch, d_inner, d_state)
+    g = {"dx": np.empty_like(x), "ddelta": np.empty_like(x), "dA": np.empty_like(A), "dB": np.empty_like(B),
+         "dC": np.empty_like(C), "dh0": np.empty((batch, d_inner, d_state))}
+    if D is not None:
+        g["dD"] = np.empty(d_inner)
+    if z is not None:
+        g["dz"] = np.empty_like(x)
+    if delta_softplus:
+        g["d_dt_bias"] = np.empty(d_inner)
+    rc = lib.ssm_oracle_scan_bwd_f64(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dt_bias), _ptr(dy),
+        _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+        _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g["dh0"]), _ptr(g.get("d_dt_bias")), batch, seqlen, d_inner,
+        d_state, 1 if exact_zoh else 0, 1 if delta_softplus else 0)
+    if rc != 0:
+        raise ValueError("oracle scan_bwd rejected its arguments (%d)" % rc)
+    return g
 
 
 def scan_channels(inputs, channels, *, exact_zoh=False, delta_softplus=False):

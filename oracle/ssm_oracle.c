@@ -206,4 +206,171 @@ int ssm_oracle_conv1d_f64(const double* x, const double* w, const double* bias, 
   return ORACLE_OK;
 }
 
-int ssm_oracle_version(void) { return 2; }
+/*
+ * d/d(a) of the exact-ZOH input coefficient coef(dt, a) = (exp(dt a) - 1)/a
+ * (the a -> 0 limit being dt).  With y = dt*a and phi1(y) = (e^y - 1)/y,
+ * coef = dt*phi1(y), so d coef/d a = dt^2 * phi1'(y), where
+ *     phi1'(y) = (y e^y - e^y + 1) / y^2 = sum_{k>=1} k y^(k-1) / (k+1)!.
+ * The closed form cancels badly for small |y|; there the series is summed.
+ */
+static double oracle_dcoef_da(double dt, double a) {
+  double y = dt * a;
+  double d1;
+  if (fabs(y) < 0.5) {
+    double term = 0.5; /* k = 1: 1 * y^0 / 2! */
+    double fact = 2.0; /* (k+1)! */
+    double ypow = 1.0;
+    d1 = 0.0;
+    for (int k = 1; k <= 30; ++k) {
+      fact = (k == 1) ? 2.0 : fact * (double)(k + 1);
+      term = (double)k * ypow / fact;
+      d1 += term;
+      ypow *= y;
+    }
+  } else {
+    d1 = (y * exp(y) - expm1(y)) / (y * y);
+  }
+  return dt * dt * d1;
+}
+
+/*
+ * Reverse-mode gradient of the full-sequence scan above (same input_mode /
+ * delta_mode meanings), for the scalar loss
+ *     L = sum(dy * y) + sum(dh_last * h_last).
+ * It is the chain rule applied to the recurrence, taken backwards in time:
+ * training back-propagates along the time axis through the scan ("SSMs for
+ * long-document QA" (pwwt.cn/news/5168881), sections 3.2-3.3, which keep a
+ * few states and recompute the intermediate ones for the backward pass;
+ * "Deriving and implementing Mamba from scratch" (dpshk.com/news/3333417),
+ * section 5.3, whose fused scan keeps what the backward pass needs).  Here
+ * every state of the channel is kept, which is the plain definition.
+ * Per channel (b, d), with lam[n] = dL/dh_t[n]:
+ *     lam <- dh_last;  for t = L-1 .. 0:
+ *        ypre = sum_n C h_t + D x;  g = dy * silu(z)  (dy if no gate)
+ *        dz   = dy * ypre * silu'(z);  dD += g x;  dx = g D
+ *        lam += g C_t;  dC_t += g h_t
+ *        h_t  = abar h_{t-1} + bbar x   with abar = exp(dt a), bbar = dt B
+ *               (exact ZOH: bbar = coef(dt, a) B)
+ *        ddt += lam (a abar h_{t-1} + d bbar/d dt * x)
+ *        dA  += lam (dt abar h_{t-1} + d bbar/d a * x)
+ *        dB_t += lam coef x;  dx += lam coef B
+ *        lam  = abar lam
+ *     dh0 = lam
+ * With delta_mode 1 the returned ddelta is d/d(raw) = ddt * sigmoid(raw + bias)
+ * and d_dt_bias[d] accumulates the same quantity.
+ *
+ * Outputs: dx, ddelta, dz (if z), shaped like x; dA [d_inner][d_state];
+ * dB, dC [batch][seqlen][d_state]; dD [d_inner] (if D); dh0 [batch][d_inner]
+ * [d_state] (nullable); d_dt_bias [d_inner] (required with delta_mode 1).
+ * dA, dB, dC, dD and d_dt_bias are sums over every channel / row that uses
+ * them; they are zeroed here first.
+ */
+int ssm_oracle_scan_bwd_f64(const double* x, const double* delta, const double* A, const double* B, const double* C,
+                            const double* D, const double* z, const double* h0, const double* dt_bias,
+                            const double* dy, const double* dh_last, double* dx, double* ddelta, double* dA,
+                            double* dB, double* dC, double* dD, double* dz, double* dh0, double* d_dt_bias,
+                            int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int input_mode,
+                            int delta_mode) {
+  if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return ORACLE_BAD_ARG;
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0) return ORACLE_BAD_ARG;
+  if (input_mode != 0 && input_mode != 1) return ORACLE_BAD_ARG;
+  if (delta_mode != 0 && delta_mode != 1) return ORACLE_BAD_ARG;
+  if (delta_mode == 1 && (!dt_bias || !d_dt_bias)) return ORACLE_BAD_ARG;
+  if ((D && !dD) || (z && !dz)) return ORACLE_BAD_ARG;
+  const int64_t N = d_state;
+  for (int64_t i = 0; i < d_inner * N; ++i) dA[i] = 0.0;
+  for (int64_t i = 0; i < batch * seqlen * N; ++i) dB[i] = dC[i] = 0.0;
+  for (int64_t i = 0; i < d_inner; ++i) {
+    if (dD) dD[i] = 0.0;
+    if (d_dt_bias) d_dt_bias[i] = 0.0;
+  }
+  /* hs[(t+1)*N + n] = h_t[n], with hs[0..N) = h_{-1} = h0. */
+  double* hs = (double*)malloc((size_t)(seqlen + 1) * (size_t)N * sizeof(double));
+  double* lam = (double*)malloc((size_t)N * sizeof(double));
+  if (!hs || !lam) {
+    free(hs);
+    free(lam);
+    return ORACLE_BAD_ARG;
+  }
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < d_inner; ++d) {
+      const double* Arow = A + d * N;
+      const double bias = dt_bias ? dt_bias[d] : 0.0;
+      const double Dv = D ? D[d] : 0.0;
+      /* Forward, keeping every state. */
+      for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * d_inner + d) * N + n] : 0.0;
+      for (int64_t t = 0; t < seqlen; ++t) {
+        const int64_t io = (b * seqlen + t) * d_inner + d;
+        double dt = delta[io];
+        if (delta_mode == 1) dt = oracle_softplus(dt + bias);
+        const double xv = x[io];
+        const double* Bt = B + (b * seqlen + t) * N;
+        for (int64_t n = 0; n < N; ++n) {
+          double a = Arow[n];
+          double coef = (input_mode == 1) ? ((a != 0.0) ? expm1(dt * a) / a : dt) : dt;
+          hs[(t + 1) * N + n] = exp(dt * a) * hs[t * N + n] + coef * Bt[n] * xv;
+        }
+      }
+      /* Backward. */
+      for (int64_t n = 0; n < N; ++n) lam[n] = dh_last ? dh_last[(b * d_inner + d) * N + n] : 0.0;
+      for (int64_t t = seqlen - 1; t >= 0; --t) {
+        const int64_t io = (b * seqlen + t) * d_inner + d;
+        const double raw = delta[io];
+        const double dt = (delta_mode == 1) ? oracle_softplus(raw + bias) : raw;
+        const double xv = x[io];
+        const double* Bt = B + (b * seqlen + t) * N;
+        const double* Ct = C + (b * seqlen + t) * N;
+        const double* ht = hs + (t + 1) * N;
+        const double* hp = hs + t * N;
+        double ypre = Dv * xv;
+        for (int64_t n = 0; n < N; ++n) ypre += Ct[n] * ht[n];
+        double g = dy[io];
+        if (z) {
+          const double zv = z[io];
+          const double sg = 1.0 / (1.0 + exp(-zv));
+          g = dy[io] * zv * sg;
+          dz[io] = dy[io] * ypre * sg * (1.0 + zv * (1.0 - sg));
+        }
+        if (dD) dD[d] += g * xv;
+        double dxv = g * Dv;
+        double ddt = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = Arow[n];
+          const double abar = exp(dt * a);
+          double coef, dcoef_ddt, dcoef_da;
+          if (input_mode == 1) {
+            coef = (a != 0.0) ? expm1(dt * a) / a : dt;
+            dcoef_ddt = abar;
+            dcoef_da = oracle_dcoef_da(dt, a);
+          } else {
+            coef = dt;
+            dcoef_ddt = 1.0;
+            dcoef_da = 0.0;
+          }
+          lam[n] += g * Ct[n];
+          dC[(b * seqlen + t) * N + n] += g * ht[n];
+          ddt += lam[n] * (a * abar * hp[n] + dcoef_ddt * Bt[n] * xv);
+          dA[d * N + n] += lam[n] * (dt * abar * hp[n] + dcoef_da * Bt[n] * xv);
+          dB[(b * seqlen + t) * N + n] += lam[n] * coef * xv;
+          dxv += lam[n] * coef * Bt[n];
+          lam[n] *= abar;
+        }
+        dx[io] = dxv;
+        if (delta_mode == 1) {
+          const double sg = 1.0 / (1.0 + exp(-(raw + bias)));
+          ddelta[io] = ddt * sg;
+          d_dt_bias[d] += ddt * sg;
+        } else {
+          ddelta[io] = ddt;
+        }
+      }
+      if (dh0)
+        for (int64_t n = 0; n < N; ++n) dh0[(b * d_inner + d) * N + n] = lam[n];
+    }
+  }
+  free(hs);
+  free(lam);
+  return ORACLE_OK;
+}
+
+int ssm_oracle_version(void) { return 3; }
