@@ -1,10 +1,14 @@
 /*
  * ssm_scan.h -- C ABI of the MI355X (gfx950) selective-scan library.
  *
- * Two operations, both from the Mamba selective state space model:
+ * Operations of the Mamba selective state space model:
  *
  *   ssm_scan_fwd      full-sequence selective scan (training / prefill)
  *   ssm_state_update  one recurrent step on a resident state (decode)
+ *   ssm_scan_bwd      gradient of the full-sequence scan (training)
+ *   ssm_conv1d_fwd / ssm_conv1d_update
+ *                     the causal depthwise convolution that feeds the scan,
+ *                     and its decode step
  *
  * Per batch row b, channel d and state n (A diagonal, B and C shared by all
  * channels of a row):
@@ -62,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef enum {
   SSM_DTYPE_F32 = 0,
@@ -190,6 +194,59 @@ int ssm_state_update(float* h, const void* x_t, const void* delta_t, const float
 int ssm_state_update_ex(float* h, const void* x_t, const void* delta_t, const float* A, const void* B_t,
                         const void* C_t, const float* D, const void* z_t, void* y_t, int64_t batch, int64_t d_inner,
                         int64_t d_state, int32_t io_dtype, uint32_t flags, const float* dt_bias, void* stream);
+
+/*
+ * Workspace bytes ssm_scan_bwd needs for these sizes (state checkpoints every
+ * 8 steps plus per-tile partial sums: about 8 bytes per (b, t, d) element for
+ * d_state 16).  Returns (size_t)-1 for invalid or unsupported sizes.  Pure
+ * host computation.
+ */
+size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state);
+
+/*
+ * Gradient of ssm_scan_fwd (the training backward pass).  Training
+ * back-propagates through the scan along time, recomputing intermediate
+ * states from a few kept ones ("SSMs for long-document QA"
+ * (pwwt.cn/news/5168881), sections 3.2-3.3; "Deriving and implementing Mamba
+ * from scratch" (dpshk.com/news/3333417), section 5.3).
+ *
+ * For the forward call with the same x, delta, A, B, C, D, z, h0 (and
+ * dt_bias, flags) and the scalar loss
+ *     L = sum(dy * y) + sum(dh_last * h_last),
+ * writes the derivative of L with respect to every input.  The states are
+ * recomputed from the inputs (nothing of the forward call is needed).
+ *
+ *   x, delta, A, B, C, D, z, h0, dt_bias : as for ssm_scan_fwd_ex.
+ *   dy          : [batch][seqlen][d_inner] io_dtype, gradient of y.
+ *   dh_last     : [batch][d_inner][d_state] fp32 gradient of h_last, or NULL for 0.
+ *   dx, ddelta  : [batch][seqlen][d_inner] io_dtype.  ddelta is taken with
+ *                 respect to the delta argument as passed: the raw projection
+ *                 when SSM_FLAG_DELTA_SOFTPLUS is set.
+ *   dz          : [batch][seqlen][d_inner] io_dtype; required when z is given,
+ *                 ignored otherwise.
+ *   dA          : [d_inner][d_state] fp32, summed over batch rows and time.
+ *   dB, dC      : [batch][seqlen][d_state] fp32, summed over channels.
+ *   dD          : [d_inner] fp32; required when D is given, ignored otherwise.
+ *   dh0         : [batch][d_inner][d_state] fp32 gradient of the initial state
+ *                 (of zeros when h0 is NULL), or NULL.
+ *   d_dt_bias   : [d_inner] fp32; required with SSM_FLAG_DELTA_SOFTPLUS.
+ *   flags       : 0 or SSM_FLAG_DELTA_SOFTPLUS (SSM_FLAG_EXACT_ZOH returns
+ *                 SSM_ERR_UNSUPPORTED).
+ *   d_state     : 2, 4, 8 or 16.
+ *   workspace   : at least ssm_scan_bwd_workspace_size() bytes, 256-byte
+ *                 aligned; contents on entry ignored.
+ * Every output is overwritten, not accumulated.  Outputs must not overlap
+ * each other, any input or the workspace.  Sums over channels, time and
+ * batch rows are taken in a fixed order: results are bitwise reproducible
+ * for a given device and sizes.  Sizes, alignment, error codes and the
+ * empty cases follow ssm_scan_fwd (with seqlen 0: dA, dD, d_dt_bias are 0
+ * and dh0 = dh_last).
+ */
+int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* h0, const float* dt_bias, const void* dy, const float* dh_last,
+                 void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* dh0,
+                 float* d_dt_bias, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                 int32_t io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Causal depthwise conv1d over time, optionally followed by SiLU: the step

@@ -54,6 +54,8 @@ SIGNATURES = {
     "ssm_scan_fwd_ex": ([_P] * 10 + [_I64] * 4 + [_I32, ctypes.POINTER(ScanOpts), _P, _SZ, _P], ctypes.c_int),
     "ssm_state_update": ([_P] * 9 + [_I64] * 3 + [_I32, _P], ctypes.c_int),
     "ssm_state_update_ex": ([_P] * 9 + [_I64] * 3 + [_I32, _U32, _P, _P], ctypes.c_int),
+    "ssm_scan_bwd_workspace_size": ([_I64, _I64, _I64, _I64], _SZ),
+    "ssm_scan_bwd": ([_P] * 20 + [_I64] * 4 + [_I32, _U32, _P, _SZ, _P], ctypes.c_int),
     "ssm_conv1d_fwd": ([_P] * 6 + [_I64] * 4 + [_I32, _I32, _P], ctypes.c_int),
     "ssm_conv1d_update": ([_P] * 5 + [_I64] * 3 + [_I32, _I32, _P], ctypes.c_int),
 }
@@ -191,6 +193,60 @@ def ssm_state_update(h, x_t, delta_t, A, B_t, C_t, D=None, z_t=None, *, y_t=None
     if rc != SSM_OK:
         raise SsmError(rc, "ssm_state_update")
     return y_t
+
+
+def scan_bwd_workspace_size(batch, seqlen, d_inner, d_state) -> int:
+    n = load_library().ssm_scan_bwd_workspace_size(batch, seqlen, d_inner, d_state)
+    if n == ctypes.c_size_t(-1).value:
+        raise SsmError(SSM_ERR_BAD_DIM, "ssm_scan_bwd_workspace_size")
+    return n
+
+
+def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, flags=0, dt_bias=None,
+                 want_dh0=True, grads=None, workspace=None, stream=None):
+    """Gradient of ssm_scan_fwd for L = sum(dy * y) + sum(dh_last * h_last).
+
+    Returns a dict with dx, ddelta (w.r.t. the delta argument as passed), dA,
+    dB, dC (fp32), and dD, dz, dh0, d_dt_bias when D, z, want_dh0, the softplus
+    flag are used.  Outputs are allocated unless given in ``grads``.
+    """
+    import torch
+    batch, seqlen, d_inner = x.shape
+    d_state = A.shape[1]
+    dt = _io_dtype(x)
+    dev = x.device
+    g = dict(grads or {})
+    f32 = dict(dtype=torch.float32, device=dev)
+    if "dx" not in g:
+        g["dx"] = torch.empty_like(x)
+    if "ddelta" not in g:
+        g["ddelta"] = torch.empty_like(x)
+    if "dA" not in g:
+        g["dA"] = torch.empty((d_inner, d_state), **f32)
+    if "dB" not in g:
+        g["dB"] = torch.empty((batch, seqlen, d_state), **f32)
+    if "dC" not in g:
+        g["dC"] = torch.empty((batch, seqlen, d_state), **f32)
+    if D is not None and "dD" not in g:
+        g["dD"] = torch.empty((d_inner,), **f32)
+    if z is not None and "dz" not in g:
+        g["dz"] = torch.empty_like(x)
+    if want_dh0 and "dh0" not in g:
+        g["dh0"] = torch.empty((batch, d_inner, d_state), **f32)
+    if (flags & SSM_FLAG_DELTA_SOFTPLUS) and "d_dt_bias" not in g:
+        g["d_dt_bias"] = torch.empty((d_inner,), **f32)
+    ws_bytes = scan_bwd_workspace_size(batch, seqlen, d_inner, d_state)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().ssm_scan_bwd(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dt_bias), _ptr(dy),
+        _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+        _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("dh0")), _ptr(g.get("d_dt_bias")), batch, seqlen, d_inner,
+        d_state, dt, flags, _ptr(workspace), ws_have, _stream(stream))
+    if rc != SSM_OK:
+        raise SsmError(rc, "ssm_scan_bwd")
+    return g
 
 
 def ssm_conv1d_fwd(x, w, bias=None, state_in=None, *, y=None, state_out=None, want_state=True, silu=True,

@@ -245,6 +245,106 @@ int update_impl(float* h, const void* x_t, const void* delta_t, const float* A, 
   return ssm::launch_update(p) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+bool bwd_d_state_ok(int64_t n) { return n == 2 || n == 4 || n == 8 || n == 16; }
+
+// Floats of backward workspace, or -1 when a size overflows.
+int64_t bwd_workspace_floats(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  const int64_t tiles = (d_inner + 63) / 64;
+  const int64_t nblk = (seqlen + ssm::kBwdBlock - 1) / ssm::kBwdBlock;
+  int64_t a, b, c;
+  // Largest sections: checkpoints and per-tile partials; the rest are smaller.
+  if (!mul3(batch, nblk, d_state, &a) || __builtin_mul_overflow(a, d_inner, &a)) return -1;
+  if (!mul3(tiles, batch, seqlen, &b) || __builtin_mul_overflow(b, 2 * d_state, &b)) return -1;
+  if (!mul3(batch, d_inner, d_state, &c)) return -1;
+  if (a > INT64_MAX / 8 || b > INT64_MAX / 8 || c > INT64_MAX / 8) return -1;
+  int64_t total;
+  ssm::bwd_workspace_layout(nullptr, batch, seqlen, d_inner, d_state, &total);
+  return total;
+}
+
+int bwd_impl(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+             const void* z, const float* h0, const float* dt_bias, const void* dy, const float* dh_last, void* dx,
+             void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* dh0, float* d_dt_bias,
+             int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int32_t io_dtype, uint32_t flags,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(batch, seqlen, d_inner, d_state);
+  if (rc != SSM_OK) return rc;
+  if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
+  if (!bwd_d_state_ok(d_state)) return SSM_ERR_UNSUPPORTED;
+  if (flags & ~(uint32_t)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
+  const bool sp = (flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
+  if (!sp) {
+    dt_bias = nullptr;
+    d_dt_bias = nullptr;
+  }
+  if (D == nullptr) dD = nullptr;
+  if (z == nullptr) dz = nullptr;
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  int64_t n_io, n_bc, n_h;
+  if (!mul3(batch, seqlen, d_inner, &n_io) || !mul3(batch, seqlen, d_state, &n_bc) ||
+      !mul3(batch, d_inner, d_state, &n_h))
+    return SSM_ERR_BAD_DIM;
+  int64_t b_io, b_bc, b_bc32, b_h;
+  if (__builtin_mul_overflow(n_io, es, &b_io) || __builtin_mul_overflow(n_bc, es, &b_bc) ||
+      __builtin_mul_overflow(n_bc, (int64_t)4, &b_bc32) || __builtin_mul_overflow(n_h, (int64_t)4, &b_h))
+    return SSM_ERR_BAD_DIM;
+  const int64_t b_a = d_inner * d_state * 4, b_d = d_inner * 4;
+
+  // Required pointers.
+  if (n_io > 0 && (x == nullptr || delta == nullptr || dy == nullptr || dx == nullptr || ddelta == nullptr))
+    return SSM_ERR_NULL_ARG;
+  if (n_io > 0 && (B == nullptr || C == nullptr || dB == nullptr || dC == nullptr)) return SSM_ERR_NULL_ARG;
+  if (b_a > 0 && (A == nullptr || dA == nullptr)) return SSM_ERR_NULL_ARG;
+  if (D != nullptr && d_inner > 0 && dD == nullptr) return SSM_ERR_NULL_ARG;
+  if (z != nullptr && n_io > 0 && dz == nullptr) return SSM_ERR_NULL_ARG;
+  if (sp && d_inner > 0 && (dt_bias == nullptr || d_dt_bias == nullptr)) return SSM_ERR_NULL_ARG;
+
+  // Alignment.
+  if (!aligned(x, es) || !aligned(delta, es) || !aligned(z, es) || !aligned(dy, es) || !aligned(dx, es) ||
+      !aligned(ddelta, es) || !aligned(dz, es))
+    return SSM_ERR_MISALIGNED;
+  const void* f4[] = {A, B, C, D, h0, dt_bias, dh_last, dA, dB, dC, dD, dh0, d_dt_bias};
+  for (const void* q : f4)
+    if (!aligned(q, 4)) return SSM_ERR_MISALIGNED;
+
+  // Aliasing: no output overlaps an input, another output or the workspace.
+  const void* ins[] = {x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last};
+  const int64_t inb[] = {b_io, b_io, b_a, b_bc, b_bc, D ? b_d : 0, z ? b_io : 0, h0 ? b_h : 0,
+                         dt_bias ? b_d : 0, b_io, dh_last ? b_h : 0};
+  const void* outs[] = {dx, ddelta, dA, dB, dC, dD, dz, dh0, d_dt_bias};
+  const int64_t outb[] = {b_io, b_io, b_a, b_bc32, b_bc32, dD ? b_d : 0, dz ? b_io : 0, dh0 ? b_h : 0,
+                          d_dt_bias ? b_d : 0};
+  for (int o = 0; o < 9; ++o) {
+    for (int k = 0; k < 11; ++k)
+      if (overlap(outs[o], outb[o], ins[k], inb[k])) return SSM_ERR_ALIAS;
+    for (int k = o + 1; k < 9; ++k)
+      if (overlap(outs[o], outb[o], outs[k], outb[k])) return SSM_ERR_ALIAS;
+  }
+
+  const int64_t floats = bwd_workspace_floats(batch, seqlen, d_inner, d_state);
+  if (floats < 0) return SSM_ERR_BAD_DIM;
+  const int64_t need = floats * 4;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < (size_t)need) return SSM_ERR_WORKSPACE;
+    if (!aligned(workspace, kWorkspaceAlign)) return SSM_ERR_MISALIGNED;
+    for (int k = 0; k < 11; ++k)
+      if (overlap(workspace, need, ins[k], inb[k])) return SSM_ERR_ALIAS;
+    for (int k = 0; k < 9; ++k)
+      if (overlap(workspace, need, outs[k], outb[k])) return SSM_ERR_ALIAS;
+  }
+  const int64_t tiles = (d_inner + 63) / 64;
+  if (batch * tiles > INT32_MAX || (n_bc * 2 + 255) / 256 > INT32_MAX || (d_inner * d_state + 255) / 256 > INT32_MAX)
+    return SSM_ERR_BAD_DIM;
+
+  if (d_inner == 0) return SSM_OK;
+  float* ws = static_cast<float*>(workspace);
+  const ssm::BwdWorkspace lay = ssm::bwd_workspace_layout(ws, batch, seqlen, d_inner, d_state, nullptr);
+  ssm::BwdLaunch p{x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0,
+                   d_dt_bias, flags, batch, seqlen, d_inner, (int32_t)d_state, io_dtype == SSM_DTYPE_BF16,
+                   static_cast<hipStream_t>(stream)};
+  return ssm::launch_scan_bwd(p, lay) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 int conv_impl(const void* x, const float* w, const float* bias, const float* state_in, void* y, float* state_out,
               int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_conv, int32_t io_dtype, int32_t apply_silu,
               void* stream, bool update) {
@@ -302,6 +402,22 @@ int ssm_conv1d_update(float* state, const void* x_t, const float* w, const float
   return conv_impl(x_t, w, bias, nullptr, y_t, state, batch, 1, d_inner, d_conv, io_dtype, apply_silu, stream, true);
 }
 
+
+size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  if (check_dims(batch, seqlen, d_inner, d_state) != SSM_OK || !bwd_d_state_ok(d_state)) return (size_t)-1;
+  const int64_t floats = bwd_workspace_floats(batch, seqlen, d_inner, d_state);
+  if (floats < 0) return (size_t)-1;
+  return (size_t)floats * 4;
+}
+
+int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* h0, const float* dt_bias, const void* dy, const float* dh_last,
+                 void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* dh0,
+                 float* d_dt_bias, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                 int32_t io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, d_dt_bias,
+                  batch, seqlen, d_inner, d_state, io_dtype, flags, workspace, workspace_bytes, stream);
+}
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 

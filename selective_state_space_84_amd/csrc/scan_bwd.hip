@@ -1,0 +1,572 @@
+// Backward pass (gradient) of the selective scan on gfx950 (MI355X).
+//
+// For the loss L = sum(dy * y) + sum(dh_last * h_last), with lam_t[n] =
+// dL/dh_t[n] (the adjoint of the state), the chain rule on
+//   h_t = abar_t h_{t-1} + dt_t B_t x_t,   abar_t = exp(dt_t A)
+//   y_t = (sum_n C_t h_t + D x_t) * silu(z_t)
+// runs backwards in time:
+//   g_t    = dy_t silu(z_t)                         (gradient of the pre-gate output)
+//   lam_t  = abar_{t+1} lam_{t+1} + g_t C_t          (starting from dh_last)
+//   dx_t   = g_t D + dt_t sum_n lam_t B_t
+//   ddt_t  = sum_n lam_t (A abar_t h_{t-1} + B_t x_t)
+//   dA    += lam_t dt_t abar_t h_{t-1}     dB_t += lam_t dt_t x_t   (summed over channels)
+//   dC_t  += g_t h_t (summed over channels)   dD += g_t x_t   dz_t = dy_t ypre_t silu'(z_t)
+//   dh0    = abar_0 lam_0
+// With a softplus step, ddt is carried through softplus' derivative (the
+// logistic sigmoid) to the raw input and summed per channel into d_dt_bias.
+// Training back-propagates through the scan along time, keeping a few states
+// and recomputing the intermediate ones ("SSMs for long-document QA"
+// (pwwt.cn/news/5168881), sections 3.2-3.3; "Deriving and implementing Mamba
+// from scratch" (dpshk.com/news/3333417), section 5.3: the fused scan keeps
+// only what the backward pass needs).
+//
+// Mapping onto CDNA4 (lane = channel, as in the forward sweep):
+//   1. k_bwd_ckpt: a forward sweep that stores the state at the start of every
+//      block of kBB = 8 steps: ckpt[b][k][n][d], so each state row is one
+//      coalesced 256-byte line per wave.
+//   2. k_bwd_sweep: one wave per (batch row, 64-channel tile) walks the blocks
+//      from last to first.  A block is recomputed forward from its checkpoint,
+//      keeping abar * h_{t-1} for its steps in VGPRs (the recurrence's inputs
+//      are not invertible in a stable way, so states are never run backwards),
+//      then walked backwards with lam in VGPRs.  B_t and C_t are wave-uniform
+//      and come through scalar loads.  dB_t and dC_t are sums over the 64
+//      channels of the wave: each lane writes its per-state terms to LDS as
+//      rows of a [state-step][lane] table and lane r then adds up row r with
+//      16-byte reads (a transpose-and-add: per state and step, one LDS write
+//      and a sixteenth of a row read, instead of a 6-level cross-lane tree).
+//      The per-tile sums go to a partial buffer.  dA, dD and the dt-bias
+//      gradient accumulate per lane over time and are written per batch row.
+//   3. k_bwd_reduce_bc / k_bwd_reduce_params: sum the partials over tiles (dB,
+//      dC) and over batch rows (dA, dD, d_dt_bias) in a fixed order, so the
+//      result does not depend on scheduling.
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+#include <type_traits>
+
+namespace ssm {
+namespace {
+
+constexpr int kBB = kBwdBlock;  // steps per checkpoint block
+constexpr int kRedStride = 68;  // LDS row stride in floats (64 lanes + 4 pad: row reads stay conflict-free)
+
+struct BwdDims {
+  int64_t batch, seqlen, d_inner;
+  int32_t tiles, nblk;
+};
+
+__device__ __forceinline__ float sigmoid(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
+
+// A wave-uniform pointer re-read through readfirstlane: the compiler then
+// treats it as an opaque SGPR value.  Row pointers that move by a fixed
+// amount per block are passed through this so that loop strength reduction
+// does not turn "SGPR base + 32-bit lane offset" into one 64-bit per-lane
+// pointer per tensor and step (which would hold ~100 VGPRs).
+// The result is typed as a global-memory pointer, so loads and stores
+// through it stay global (SGPR base + VGPR offset) instead of flat.
+typedef char __attribute__((address_space(1))) gchar;
+__device__ __forceinline__ gchar* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<gchar*>(((uint64_t)hi << 32) | lo);
+}
+template <typename T>
+__device__ __forceinline__ float gld(const gchar* base, uint32_t off) {
+  return io_to_f32(*reinterpret_cast<const T __attribute__((address_space(1)))*>(base + off));
+}
+template <typename T>
+__device__ __forceinline__ void gst(gchar* base, uint32_t off, float v) {
+  T bits;
+  io_store(&bits, v);
+  *reinterpret_cast<T __attribute__((address_space(1)))*>(base + off) = bits;
+}
+
+// ckpt[b][k][n][d] = state before step k * kBB, k = 0 .. nblk-1.
+template <typename T, int N, int MODE>
+__global__ void __launch_bounds__(64)
+    k_bwd_ckpt(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
+               const T* __restrict__ B, const float* __restrict__ h0, const float* __restrict__ dt_bias,
+               float* __restrict__ ckpt, const BwdDims dm) {
+  const int lane = threadIdx.x;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = bid % dm.tiles;
+  const int64_t b = bid / dm.tiles;
+  const int64_t DI = dm.d_inner, L = dm.seqlen;
+  const int64_t d = (int64_t)tile * 64 + lane;
+  const bool dvalid = d < DI;
+  const int64_t dc = dvalid ? d : DI - 1;
+
+  float Al2[N], h[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    Al2[n] = A[dc * N + n] * kLog2e;
+    h[n] = h0 != nullptr ? h0[(b * DI + dc) * N + n] : 0.f;
+  }
+  const float dtb = (MODE & 1) ? dt_bias[dc] : 0.f;
+  const T* xc = x + b * L * DI + dc;
+  const T* dlc = delta + b * L * DI + dc;
+  const T* Bb = B + b * L * N;
+  float* cp = ckpt + b * dm.nblk * N * DI + d;
+
+  // Only blocks 0 .. nblk-2 are stepped through (the state after the last
+  // block is not needed), and all of them are full.
+  T xn[kBB], dn[kBB];
+  auto fetch = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < kBB; ++i) {
+      const int64_t o = ((int64_t)k * kBB + i) * DI;
+      xn[i] = xc[o];
+      dn[i] = dlc[o];
+    }
+  };
+  if (dm.nblk > 1) fetch(0);
+  for (int k = 0; k < dm.nblk; ++k) {
+    if (dvalid) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) cp[((int64_t)k * N + n) * DI] = h[n];
+    }
+    if (k + 1 >= dm.nblk) break;
+    T xr[kBB], dr[kBB];
+#pragma unroll
+    for (int i = 0; i < kBB; ++i) {
+      xr[i] = xn[i];
+      dr[i] = dn[i];
+    }
+    if (k + 2 < dm.nblk) fetch(k + 1);
+    const T* Bk = Bb + (int64_t)k * kBB * N;
+#pragma unroll
+    for (int i = 0; i < kBB; ++i) {
+      StateRow<T, N> br;
+      br.load(Bk + i * N);
+      float dt = io_to_f32(dr[i]);
+      if (MODE & 1) dt = softplus(dt + dtb);
+      const float wx = dt * io_to_f32(xr[i]);
+#pragma unroll
+      for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(hw_exp2(dt * Al2[n]), h[n], wx * br.get(n));
+    }
+  }
+}
+
+// Steps of abar * h_{t-1} a lane keeps in VGPRs at once.  With 16 states a
+// block is handled as two halves, the second one first: each half is
+// reached by a forward pass from the block's checkpoint that keeps w only
+// for that half (so the second half's pass also steps through the first
+// half: one extra decay + FMA per state for half of the steps), then walked
+// back.  This holds 64 values instead of 128, which lets two waves share a
+// SIMD.
+template <int N>
+constexpr int bwd_sub() {
+  return N * kBB <= 64 ? kBB : 64 / N;
+}
+
+template <typename T, int N, int MODE>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+    k_bwd_sweep(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
+                const T* __restrict__ B, const T* __restrict__ C, const float* __restrict__ D,
+                const T* __restrict__ z, const T* __restrict__ dy, const float* __restrict__ dh_last,
+                const float* __restrict__ dt_bias, const float* __restrict__ ckpt, T* __restrict__ dx,
+                T* __restrict__ ddelta, T* __restrict__ dz, float* __restrict__ dh0, float* __restrict__ part_bc,
+                float* __restrict__ part_a, float* __restrict__ part_d, float* __restrict__ part_t,
+                const BwdDims dm) {
+  constexpr int SUB = bwd_sub<N>();                   // steps of w held at once
+  constexpr int NSUB = kBB / SUB;                     // sub-blocks per block
+  constexpr int GS = (64 / N) < SUB ? (64 / N) : SUB;  // steps per LDS reduction group
+  constexpr int ROWS = GS * N;
+  static_assert(kBB % SUB == 0 && SUB % GS == 0 && ROWS <= 64, "bad block split");
+  __shared__ __align__(16) float red[ROWS * kRedStride];
+
+  const int lane = threadIdx.x;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = bid % dm.tiles;
+  const int64_t b = bid / dm.tiles;
+  const int64_t DI = dm.d_inner, L = dm.seqlen;
+  const int64_t d = (int64_t)tile * 64 + lane;
+  const bool dvalid = d < DI;
+  const int64_t dc = dvalid ? d : DI - 1;
+  const bool has_z = z != nullptr;
+
+  // Lanes past d_inner run on a copy of the last channel with g = 0 and
+  // lam = 0, so every term they add to the channel sums is zero.
+  float Al2[N], lam[N], gA[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    Al2[n] = A[dc * N + n] * kLog2e;
+    lam[n] = (dvalid && dh_last != nullptr) ? dh_last[(b * DI + d) * N + n] : 0.f;
+    gA[n] = 0.f;
+  }
+  const float Dv = D != nullptr ? D[dc] : 0.f;
+  const float dtb = (MODE & 1) ? dt_bias[dc] : 0.f;
+  float accD = 0.f, accT = 0.f;
+
+  // Addressing (as in the forward sweep): the io tensors share one layout,
+  // so a block of kBB rows is reached from one wave-uniform row pointer per
+  // tensor (SGPRs) plus per-lane 32-bit byte offsets voff[i] computed once.
+  const int64_t cbase = (int64_t)tile * 64;
+  const int lc = (int)(dc - cbase);
+  const uint32_t row_bytes = (uint32_t)(DI * (int64_t)sizeof(T));
+  uint32_t voff[kBB];
+#pragma unroll
+  for (int i = 0; i < kBB; ++i) voff[i] = (uint32_t)lc * (uint32_t)sizeof(T) + (uint32_t)i * row_bytes;
+  auto rowp = [&](const void* base, int64_t t) {
+    return uniform_ptr(reinterpret_cast<const char*>(base) + ((b * L + t) * DI + cbase) * (int64_t)sizeof(T));
+  };
+  auto ld = [](const gchar* base, uint32_t off) { return gld<T>(base, off); };
+  auto st = [](gchar* base, uint32_t off, float v) { gst<T>(base, off, v); };
+  const T* Bb = B + b * L * N;
+  const T* Cb = C + b * L * N;
+  float* pbc = part_bc + ((int64_t)tile * dm.batch + b) * L * (2 * N);
+
+  // B/C rows run one step ahead through SGPRs: each step waits for its own
+  // rows (issued one step earlier), then requests the rows of the step that
+  // follows it in processing order.
+  StateRow<T, N> bq, cq;
+  auto issue = [&](int64_t t) {
+    bq.load(Bb + t * N);
+    cq.load(Cb + t * N);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto take = [&](StateRow<T, N>& bc, StateRow<T, N>& cc) {
+    bq.touch();
+    cq.touch();
+    __builtin_amdgcn_sched_barrier(0);
+    bc = bq;
+    cc = cq;
+  };
+
+  // Sum of the ROWS x 64 table over lanes; row r = (step s, state n) of the
+  // group starting at step g0 lands in the partial buffer at step
+  // t0 + g0 + s, column which + n (which = 0 for dB, N for dC).  Four
+  // 16-byte reads are in flight at a time.
+  auto reduce = [&](int64_t t0, int g0, int nt, int which) {
+    __syncthreads();
+    if (lane < ROWS) {
+      const float4* row = reinterpret_cast<const float4*>(red + lane * kRedStride);
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int q0 = 0; q0 < 16; q0 += 4) {
+        float4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = row[q0 + q];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          s0 += v[q].x;
+          s1 += v[q].y;
+          s2 += v[q].z;
+          s3 += v[q].w;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int st_ = lane / N, n = lane % N;
+      if (g0 + st_ < nt) pbc[(t0 + g0 + st_) * (2 * N) + which + n] = (s0 + s1) + (s2 + s3);
+    }
+    __syncthreads();
+  };
+
+  auto block = [&](int k) {
+    const int64_t t0 = (int64_t)k * kBB;
+    const int nt = (int)min((int64_t)kBB, L - t0);
+    const int nsub = (nt + SUB - 1) / SUB;  // sub-blocks holding steps
+    // Row offsets; past a ragged end the loads repeat the last row.
+    const uint32_t off_last = voff[0] + (uint32_t)(nt - 1) * row_bytes;
+    auto offs = [&](int i) { return i < nt ? voff[i] : off_last; };
+    float xv[kBB], dt[kBB], sg[(MODE & 1) ? kBB : 1];
+    {
+      const gchar* xb = rowp(x, t0);
+      const gchar* db = rowp(delta, t0);
+#pragma unroll
+      for (int i = 0; i < kBB; ++i) {
+        xv[i] = ld(xb, offs(i));
+        const float raw = ld(db, offs(i));
+        if (MODE & 1) {
+          const float v = raw + dtb;
+          dt[i] = softplus(v);
+          sg[i] = sigmoid(v);
+        } else {
+          dt[i] = raw;
+        }
+      }
+    }
+    const gchar* cpb = uniform_ptr(ckpt + (b * dm.nblk + k) * N * DI + cbase);
+    const uint32_t coff = (uint32_t)lc * 4u;
+
+#pragma unroll
+    for (int j = NSUB - 1; j >= 0; --j) {
+      if (j >= nsub) continue;
+      const int lo = j * SUB, hi = min(nt, lo + SUB);  // this pass covers steps [lo, hi)
+      // dy and the gate terms of this sub-block.  Loads are unconditional
+      // (zb falls back to x; tail lanes read a valid channel) and the
+      // conditions become selects, so no load waits behind a branch.
+      float g[SUB], dsz[SUB];
+      {
+        const gchar* yb = rowp(dy, t0);
+        const gchar* zb = has_z ? rowp(z, t0) : rowp(x, t0);
+#pragma unroll
+        for (int i = 0; i < SUB; ++i) {
+          const uint32_t o = offs(lo + i);
+          const float dyv = dvalid ? ld(yb, o) : 0.f;
+          const float zv = ld(zb, o);
+          const float s = sigmoid(zv);
+          g[i] = has_z ? dyv * zv * s : dyv;
+          dsz[i] = dyv * s * __builtin_fmaf(zv, 1.f - s, 1.f);
+        }
+      }
+
+      // Forward from the checkpoint to the end of this sub-block.  Steps
+      // before it only advance h; its own steps keep w = abar * h_{i-1},
+      // read out the pre-gate output (for dz) and write the rows g * h_i
+      // (for dC).  Each pass reads the steps through its own opaque copy, so
+      // the compiler cannot merge the decays of different passes (keeping
+      // them alive between passes would cost more VGPRs than recomputing).
+      float w[SUB][N];
+      float dzo[SUB];
+      float dtp[kBB];
+#pragma unroll
+      for (int i = 0; i < kBB; ++i) {
+        dtp[i] = dt[i];
+        if (i < lo + SUB) asm volatile("" : "+v"(dtp[i]));
+      }
+      {
+        float h[N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) h[n] = gld<float>(cpb + (int64_t)n * DI * 4, coff);
+#pragma unroll
+        for (int i = 0; i < lo; ++i) {
+          StateRow<T, N> br, cr;
+          take(br, cr);
+          issue(t0 + i + 1);
+          const float dtx = dtp[i] * xv[i];
+#pragma unroll
+          for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(dtx, br.get(n), hw_exp2(dtp[i] * Al2[n]) * h[n]);
+        }
+#pragma unroll
+        for (int g0 = 0; g0 < SUB; g0 += GS) {
+          if (lo + g0 >= hi) break;
+#pragma unroll
+          for (int s = 0; s < GS; ++s) {
+            const int ii = g0 + s, i = lo + ii;
+            if (i < hi) {
+              StateRow<T, N> br, cr;
+              take(br, cr);
+              issue(i + 1 < hi ? t0 + i + 1 : t0 + hi - 1);
+              const float dtx = dtp[i] * xv[i];
+              float acc = Dv * xv[i];
+#pragma unroll
+              for (int n = 0; n < N; ++n) {
+                const float wv = hw_exp2(dtp[i] * Al2[n]) * h[n];
+                w[ii][n] = wv;
+                h[n] = __builtin_fmaf(dtx, br.get(n), wv);
+                acc = __builtin_fmaf(cr.get(n), h[n], acc);
+                red[(s * N + n) * kRedStride + lane] = g[ii] * h[n];
+              }
+              dzo[ii] = acc * dsz[ii];
+            }
+          }
+          reduce(t0, lo + g0, nt, N);
+        }
+      }
+      if (has_z && dvalid) {
+        gchar* ob = rowp(dz, t0);
+#pragma unroll
+        for (int ii = 0; ii < SUB; ++ii)
+          if (lo + ii < hi) st(ob, voff[lo + ii], dzo[ii]);
+      }
+
+      // Backward through this sub-block.
+      float dxo[SUB], ddo[SUB];
+#pragma unroll
+      for (int g0 = SUB - GS; g0 >= 0; g0 -= GS) {
+        if (lo + g0 >= hi) continue;
+#pragma unroll
+        for (int s = GS - 1; s >= 0; --s) {
+          const int ii = g0 + s, i = lo + ii;
+          if (i < hi) {
+            StateRow<T, N> br, cr;
+            take(br, cr);
+            issue(i > lo ? t0 + i - 1 : (j > 0 ? t0 : (k > 0 ? t0 - kBB : t0)));
+            // The decays are recomputed here rather than kept from the
+            // forward pass (that would hold another SUB * N values in
+            // VGPRs); the empty asm keeps the compiler from merging the two
+            // computations.
+            float dti = dt[i];
+            asm volatile("" : "+v"(dti));
+            const float dtx = dti * xv[i];
+            float dd = 0.f, sb = 0.f;
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+              lam[n] = __builtin_fmaf(g[ii], cr.get(n), lam[n]);
+              const float tw = lam[n] * w[ii][n];
+              dd = __builtin_fmaf(tw, Al2[n], dd);
+              gA[n] = __builtin_fmaf(dti, tw, gA[n]);
+              sb = __builtin_fmaf(lam[n], br.get(n), sb);
+              red[(s * N + n) * kRedStride + lane] = lam[n] * dtx;
+              lam[n] *= hw_exp2(dti * Al2[n]);
+            }
+            dxo[ii] = __builtin_fmaf(g[ii], Dv, dti * sb);
+            float ddt = __builtin_fmaf(dd, kLn2, xv[i] * sb);
+            if (MODE & 1) ddt *= sg[i];
+            accT += ddt;
+            ddo[ii] = ddt;
+            accD = __builtin_fmaf(g[ii], xv[i], accD);
+          }
+        }
+        reduce(t0, lo + g0, nt, 0);
+      }
+      if (dvalid) {
+        gchar* ob = rowp(dx, t0);
+        gchar* pb = rowp(ddelta, t0);
+#pragma unroll
+        for (int ii = 0; ii < SUB; ++ii) {
+          if (lo + ii < hi) {
+            st(ob, voff[lo + ii], dxo[ii]);
+            st(pb, voff[lo + ii], ddo[ii]);
+          }
+        }
+      }
+    }
+  };
+
+  if (dm.nblk > 0) {
+    issue((int64_t)(dm.nblk - 1) * kBB);
+    for (int k = dm.nblk - 1; k >= 0; --k) block(k);
+    // Let the last row request land before the wave ends.
+    bq.touch();
+    cq.touch();
+  }
+
+  if (dvalid) {
+    if (dh0 != nullptr) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) dh0[(b * DI + d) * N + n] = lam[n];
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) part_a[(b * DI + d) * N + n] = gA[n];
+    part_d[b * DI + d] = accD;
+    part_t[b * DI + d] = accT;
+  }
+}
+
+// dB[r][n] = sum over tiles of part[tile][r][n], dC[r][n] likewise from
+// column N + n; r runs over (b, t).
+__global__ void __launch_bounds__(256) k_bwd_reduce_bc(const float* __restrict__ part, float* __restrict__ dB,
+                                                       float* __restrict__ dC, int64_t rows, int32_t N,
+                                                       int32_t tiles) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = rows * 2 * N;
+  if (i >= total) return;
+  float s = 0.f;
+  for (int t = 0; t < tiles; ++t) s += part[(int64_t)t * total + i];
+  const int64_t r = i / (2 * N);
+  const int c = (int)(i - r * 2 * N);
+  if (c < N) {
+    dB[r * N + c] = s;
+  } else {
+    dC[r * N + c - N] = s;
+  }
+}
+
+// dA[d][n], dD[d], d_dt_bias[d]: sums over batch rows.
+__global__ void __launch_bounds__(256) k_bwd_reduce_params(const float* __restrict__ part_a,
+                                                           const float* __restrict__ part_d,
+                                                           const float* __restrict__ part_t, float* __restrict__ dA,
+                                                           float* __restrict__ dD, float* __restrict__ d_dt_bias,
+                                                           int64_t batch, int64_t d_inner, int32_t N) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t na = d_inner * N;
+  if (i < na) {
+    float s = 0.f;
+    for (int64_t b = 0; b < batch; ++b) s += part_a[b * na + i];
+    dA[i] = s;
+  }
+  if (i < d_inner) {
+    if (dD != nullptr) {
+      float s = 0.f;
+      for (int64_t b = 0; b < batch; ++b) s += part_d[b * d_inner + i];
+      dD[i] = s;
+    }
+    if (d_dt_bias != nullptr) {
+      float s = 0.f;
+      for (int64_t b = 0; b < batch; ++b) s += part_t[b * d_inner + i];
+      d_dt_bias[i] = s;
+    }
+  }
+}
+
+template <typename T, int N, int MODE>
+hipError_t launch_bwd_t(const BwdLaunch& p, const BwdWorkspace& ws) {
+  const int64_t tiles = (p.d_inner + 63) / 64;
+  const BwdDims dm{p.batch, p.seqlen, p.d_inner, (int32_t)tiles, (int32_t)((p.seqlen + kBB - 1) / kBB)};
+  const T* x = static_cast<const T*>(p.x);
+  const T* dl = static_cast<const T*>(p.delta);
+  const T* Bm = static_cast<const T*>(p.B);
+  const T* Cm = static_cast<const T*>(p.C);
+  hipError_t e;
+  const unsigned waves = (unsigned)(p.batch * tiles);
+  if (waves > 0) {
+    if (dm.nblk > 0) {
+      e = launch(k_bwd_ckpt<T, N, MODE>, dim3(waves), dim3(64), 0, p.stream, x, dl, p.A, Bm, p.h0, p.dt_bias,
+                 ws.ckpt, dm);
+      if (e != hipSuccess) return e;
+    }
+    e = launch(k_bwd_sweep<T, N, MODE>, dim3(waves), dim3(64), 0, p.stream, x, dl, p.A, Bm, Cm, p.D,
+               static_cast<const T*>(p.z), static_cast<const T*>(p.dy), p.dh_last, p.dt_bias, ws.ckpt,
+               static_cast<T*>(p.dx), static_cast<T*>(p.ddelta), static_cast<T*>(p.dz), p.dh0, ws.part_bc,
+               ws.part_a, ws.part_d, ws.part_t, dm);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t rows = p.batch * p.seqlen;
+  if (rows > 0) {
+    const int64_t total = rows * 2 * N;
+    e = launch(k_bwd_reduce_bc, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, p.stream, ws.part_bc, p.dB,
+               p.dC, rows, (int32_t)N, (int32_t)tiles);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t na = p.d_inner * N;
+  if (na > 0) {
+    e = launch(k_bwd_reduce_params, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, p.stream, ws.part_a,
+               ws.part_d, ws.part_t, p.dA, p.dD, p.d_dt_bias, p.batch, p.d_inner, (int32_t)N);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T, int MODE>
+hipError_t launch_bwd_n(const BwdLaunch& p, const BwdWorkspace& ws) {
+  switch (p.d_state) {
+    case 2: return launch_bwd_t<T, 2, MODE>(p, ws);
+    case 4: return launch_bwd_t<T, 4, MODE>(p, ws);
+    case 8: return launch_bwd_t<T, 8, MODE>(p, ws);
+    case 16: return launch_bwd_t<T, 16, MODE>(p, ws);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                  int64_t* total_floats) {
+  auto up = [](int64_t v) { return (v + 63) / 64 * 64; };  // 256-byte sections
+  const int64_t tiles = (d_inner + 63) / 64;
+  const int64_t nblk = (seqlen + kBB - 1) / kBB;
+  const int64_t n_ck = up(batch * nblk * d_state * d_inner);
+  const int64_t n_bc = up(tiles * batch * seqlen * 2 * d_state);
+  const int64_t n_a = up(batch * d_inner * d_state);
+  const int64_t n_d = up(batch * d_inner);
+  BwdWorkspace ws{};
+  if (base != nullptr) {
+    ws.ckpt = base;
+    ws.part_bc = ws.ckpt + n_ck;
+    ws.part_a = ws.part_bc + n_bc;
+    ws.part_d = ws.part_a + n_a;
+    ws.part_t = ws.part_d + n_d;
+  }
+  if (total_floats != nullptr) *total_floats = n_ck + n_bc + n_a + 2 * n_d;
+  return ws;
+}
+
+hipError_t launch_scan_bwd(const BwdLaunch& p, const BwdWorkspace& ws) {
+  if (p.flags & 1u) return p.bf16 ? launch_bwd_n<uint16_t, 1>(p, ws) : launch_bwd_n<float, 1>(p, ws);
+  return p.bf16 ? launch_bwd_n<uint16_t, 0>(p, ws) : launch_bwd_n<float, 0>(p, ws);
+}
+
+}  // namespace ssm

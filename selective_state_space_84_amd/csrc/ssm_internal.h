@@ -81,6 +81,55 @@ inline int64_t scan_workspace_floats(int64_t n_chunks, int64_t states) {
   return n_chunks > 1 ? (3 * n_chunks - 2) * states : 0;
 }
 
+// Gradient of the scan (one launch sequence).  io tensors (x, delta, z, dy,
+// dx, ddelta, dz) are fp32 or bf16 according to bf16; the rest are fp32.
+struct BwdLaunch {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;        // nullable
+  const void* z;         // nullable
+  const float* h0;       // nullable
+  const float* dt_bias;  // used with SSM_FLAG_DELTA_SOFTPLUS
+  const void* dy;
+  const float* dh_last;  // nullable
+  void* dx;
+  void* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;         // nullable (required when D is given)
+  void* dz;          // nullable (required when z is given)
+  float* dh0;        // nullable
+  float* d_dt_bias;  // used with SSM_FLAG_DELTA_SOFTPLUS
+  uint32_t flags;
+  int64_t batch, seqlen, d_inner;
+  int32_t d_state;
+  bool bf16;
+  hipStream_t stream;
+};
+
+// Steps per checkpoint block of the backward pass.
+constexpr int kBwdBlock = 8;
+
+// Sections of the backward workspace (floats, each 256-byte aligned):
+//   ckpt    [batch][ceil(seqlen/8)][d_state][d_inner]  states at block starts
+//   part_bc [tiles][batch][seqlen][2*d_state]          per-tile dB | dC sums
+//   part_a  [batch][d_inner][d_state]                  per-row dA
+//   part_d, part_t [batch][d_inner]                    per-row dD, d_dt_bias
+struct BwdWorkspace {
+  float* ckpt;
+  float* part_bc;
+  float* part_a;
+  float* part_d;
+  float* part_t;
+};
+BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                  int64_t* total_floats);
+hipError_t launch_scan_bwd(const BwdLaunch& p, const BwdWorkspace& ws);
+
 hipError_t launch_scan(const ScanLaunch& p);
 template <int MODE>
 hipError_t launch_scan_mode(const ScanLaunch& p);  // one translation unit per MODE

@@ -219,6 +219,35 @@ def make_decode_inputs(batch: int, d_inner: int, d_state: int, dtype: str, steps
     return out
 
 
+def make_scan_grads(batch: int, seqlen: int, d_inner: int, d_state: int, dtype: str, seed: int,
+                    threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Upstream gradients for the scan's backward pass: dy (batch, seqlen,
+    d_inner) ~ N(0, 1) in the io type and dh_last (batch, d_inner, d_state)
+    ~ N(0, 1) fp32, from their own seed stream (drawn per batch row and
+    4096-step segment, like the inputs)."""
+    dy_kid, dh_kid = np.random.SeedSequence([seed, 0xB4C4]).spawn(2)
+    nseg = max(1, -(-seqlen // SEGMENT))
+    io_t = np.uint16 if dtype == "bf16" else np.float32
+    dy = np.empty((batch, seqlen, d_inner), dtype=io_t)
+    grand = dy_kid.spawn(batch * nseg)
+
+    def fill(task: int):
+        b, s = divmod(task, nseg)
+        t0, t1 = s * SEGMENT, min(seqlen, (s + 1) * SEGMENT)
+        if t1 > t0:
+            dy[b, t0:t1] = _to_io(np.random.default_rng(grand[task]).standard_normal((t1 - t0, d_inner)), dtype)
+
+    tasks = batch * nseg
+    if tasks > 1 and batch * seqlen * d_inner > (1 << 20):
+        with ThreadPoolExecutor(_threads(threads)) as ex:
+            list(ex.map(fill, range(tasks)))
+    else:
+        for k in range(tasks):
+            fill(k)
+    dh = round_to_f32(np.random.default_rng(dh_kid).standard_normal((batch, d_inner, d_state)))
+    return {"dy": dy, "dh_last": dh}
+
+
 def decode_inputs(cfg: DecodeConfig, steps: Optional[int] = None, threads: Optional[int] = None):
     return make_decode_inputs(cfg.batch, cfg.d_inner, cfg.d_state, cfg.dtype, steps or cfg.steps, cfg.seed, threads)
 

@@ -30,7 +30,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_messages(lib):
-    assert bd.abi_version() == 1
+    want = int(re.search(r"#define SSM_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert bd.abi_version() == want
     for code in range(-7, 1):
         assert bd.strerror(code)
     assert "unknown" in bd.strerror(-99)
@@ -159,3 +160,62 @@ def test_conv_argument_errors(lib):
     assert lib.ssm_conv1d_update(None, P0, P0 + MB, None, P0 + 2 * MB, 2, 8, 4, 1, 1, None) == bd.SSM_ERR_NULL_ARG
     assert lib.ssm_conv1d_update(P0 + 3 * MB, P0, P0 + MB, None, P0 + 2 * MB, 2, 8, 7, 1, 1, None) == \
         bd.SSM_ERR_UNSUPPORTED
+
+
+def _bwd(lib, x=P0, delta=P0 + MB, A=P0 + 2 * MB, B=P0 + 3 * MB, C=P0 + 4 * MB, D=None, z=None, h0=None,
+         dt_bias=None, dy=P0 + 5 * MB, dh_last=None, dx=P0 + 10 * MB, ddelta=P0 + 11 * MB, dA=P0 + 12 * MB,
+         dB=P0 + 13 * MB, dC=P0 + 14 * MB, dD=None, dz=None, dh0=None, d_dt_bias=None, batch=2, L=4, d=8, N=16,
+         dtype=1, flags=0, ws=P0 + 64 * MB, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.ssm_scan_bwd_workspace_size(batch, L, d, N) if batch >= 0 and L >= 0 and d >= 0 else 0
+        if ws_bytes == ctypes.c_size_t(-1).value:
+            ws_bytes = 0
+    return lib.ssm_scan_bwd(x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0,
+                            d_dt_bias, batch, L, d, N, dtype, flags, ws, ws_bytes, None)
+
+
+def test_bwd_workspace_size(lib):
+    # checkpoints every 8 steps + per-tile dB|dC partials + per-row dA, dD, d_dt_bias (256-byte sections)
+    def up(v):
+        return (v + 63) // 64 * 64
+    b, L, d, N = 3, 21, 130, 16
+    tiles, nblk = 3, 3
+    want = (up(b * nblk * N * d) + up(tiles * b * L * 2 * N) + up(b * d * N) + 2 * up(b * d)) * 4
+    assert lib.ssm_scan_bwd_workspace_size(b, L, d, N) == want
+    assert lib.ssm_scan_bwd_workspace_size(b, L, d, 32) == ctypes.c_size_t(-1).value
+    assert lib.ssm_scan_bwd_workspace_size(-1, L, d, N) == ctypes.c_size_t(-1).value
+    assert bd.scan_bwd_workspace_size(0, 0, 0, 16) == 0
+
+
+def test_bwd_argument_errors(lib):
+    assert _bwd(lib, x=None) == bd.SSM_ERR_NULL_ARG
+    assert _bwd(lib, dy=None) == bd.SSM_ERR_NULL_ARG
+    assert _bwd(lib, dx=None) == bd.SSM_ERR_NULL_ARG
+    assert _bwd(lib, dB=None) == bd.SSM_ERR_NULL_ARG
+    assert _bwd(lib, dA=None) == bd.SSM_ERR_NULL_ARG
+    # D given needs dD; z given needs dz; the softplus step needs dt_bias and d_dt_bias.
+    assert _bwd(lib, D=P0 + 6 * MB) == bd.SSM_ERR_NULL_ARG
+    assert _bwd(lib, z=P0 + 7 * MB) == bd.SSM_ERR_NULL_ARG
+    sp = bd.SSM_FLAG_DELTA_SOFTPLUS
+    assert _bwd(lib, flags=sp) == bd.SSM_ERR_NULL_ARG
+    assert _bwd(lib, flags=sp, dt_bias=P0 + 8 * MB) == bd.SSM_ERR_NULL_ARG
+    # Unsupported: exact ZOH, unknown flags, d_state outside {2,4,8,16}, dtype.
+    assert _bwd(lib, flags=bd.SSM_FLAG_EXACT_ZOH) == bd.SSM_ERR_UNSUPPORTED
+    assert _bwd(lib, flags=0x40) == bd.SSM_ERR_UNSUPPORTED
+    assert _bwd(lib, N=32) == bd.SSM_ERR_UNSUPPORTED
+    assert _bwd(lib, N=3) == bd.SSM_ERR_UNSUPPORTED
+    assert _bwd(lib, dtype=5) == bd.SSM_ERR_UNSUPPORTED
+    assert _bwd(lib, batch=-1) == bd.SSM_ERR_BAD_DIM
+    assert _bwd(lib, batch=1, L=(1 << 31) - 100, d=1, ws_bytes=0) == bd.SSM_ERR_BAD_DIM
+    # Alignment.
+    assert _bwd(lib, dx=P0 + 10 * MB + 1) == bd.SSM_ERR_MISALIGNED
+    assert _bwd(lib, dB=P0 + 13 * MB + 2) == bd.SSM_ERR_MISALIGNED
+    # Aliasing: an output over an input, two outputs over each other, the workspace over an output.
+    assert _bwd(lib, dx=P0 + 32) == bd.SSM_ERR_ALIAS
+    assert _bwd(lib, ddelta=P0 + 10 * MB + 8) == bd.SSM_ERR_ALIAS
+    assert _bwd(lib, ws=P0 + 12 * MB) == bd.SSM_ERR_ALIAS
+    # Workspace: missing, too small, misaligned.
+    assert _bwd(lib, ws=None) == bd.SSM_ERR_WORKSPACE
+    need = lib.ssm_scan_bwd_workspace_size(2, 4, 8, 16)
+    assert _bwd(lib, ws_bytes=need - 4) == bd.SSM_ERR_WORKSPACE
+    assert _bwd(lib, ws=P0 + 64 * MB + 16) == bd.SSM_ERR_MISALIGNED

@@ -1,0 +1,210 @@
+"""GPU parity of ssm_scan_bwd (the gradient of the scan) against the fp64
+oracle's reverse-mode gradient (itself pinned by finite differences), through
+the C ABI."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import floored_rel_err
+from selective_state_space_84_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+SP = 0x1  # SSM_FLAG_DELTA_SOFTPLUS
+
+# Gates on the floored relative error of every gradient (see the design doc for
+# the derivation): fp32 io: long fp32 sums over time, channels and batch rows;
+# bf16 io: dx, ddelta and dz are rounded to bf16 (2^-9 relative).
+F32_GATE = 1e-4
+BF16_GATE = 2e-2
+
+
+def _gate(dtype):
+    return F32_GATE if dtype == "f32" else BF16_GATE
+
+
+def _case(batch, L, d, N, dtype, seed, softplus=False, h0=True):
+    inp = inputs.make_scan_inputs(batch, L, d, N, dtype, seed, nonzero_h0=h0, raw_delta=softplus)
+    gr = inputs.make_scan_grads(batch, L, d, N, dtype, seed)
+    return inp, gr
+
+
+def _gpu(inp, gr, *, use_D=True, use_z=True, use_h0=True, use_dhl=True, softplus=False, want_dh0=True):
+    import torch
+    from gpu_util import to_dev, to_host_f64
+    from selective_state_space_84_amd import binding
+    d = {k: to_dev(inp.get(k)) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "dt_bias")}
+    g = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"] if use_D else None,
+                             d["z"] if use_z else None, d["h0"] if use_h0 else None, dy=to_dev(gr["dy"]),
+                             dh_last=to_dev(gr["dh_last"]) if use_dhl else None, flags=SP if softplus else 0,
+                             dt_bias=d["dt_bias"] if softplus else None, want_dh0=want_dh0)
+    torch.cuda.synchronize()
+    return {k: to_host_f64(v) for k, v in g.items()}
+
+
+def _ref(inp, gr, *, use_D=True, use_z=True, use_h0=True, use_dhl=True, softplus=False):
+    return oracle.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"] if use_D else None,
+                           inp["z"] if use_z else None, inp["h0"] if use_h0 else None,
+                           inp["dt_bias"] if softplus else None, dy=gr["dy"],
+                           dh_last=gr["dh_last"] if use_dhl else None, delta_softplus=softplus)
+
+
+def _compare(g, r, gate, keys=None, label=""):
+    errs = {}
+    for k in keys or r:
+        if k not in g:
+            continue
+        errs[k] = floored_rel_err(g[k], r[k]) if r[k].size else 0.0
+    print(label, " ".join("%s %.2e" % kv for kv in errs.items()), flush=True)
+    for k, e in errs.items():
+        assert e <= gate, (k, e)
+    return errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d_state", [2, 4, 8, 16])
+def test_bwd_ragged_all_options(lib, dtype, d_state):
+    """37 steps (ragged last block), 100 channels (ragged last tile), every
+    optional input present."""
+    inp, gr = _case(2, 37, 100, d_state, dtype, 1000 + d_state)
+    print("case bwd", dtype, d_state, flush=True)
+    _compare(_gpu(inp, gr), _ref(inp, gr), _gate(dtype), label="bwd %s N=%d" % (dtype, d_state))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_softplus_step(lib, dtype):
+    inp, gr = _case(2, 45, 130, 16, dtype, 1100, softplus=True)
+    print("case bwd softplus", dtype, flush=True)
+    g = _gpu(inp, gr, softplus=True)
+    assert "d_dt_bias" in g
+    _compare(g, _ref(inp, gr, softplus=True), _gate(dtype), label="softplus %s" % dtype)
+
+
+@pytest.mark.parametrize("L", [1, 3, 4, 5, 8, 9, 12, 16, 17])
+def test_bwd_block_edges(lib, L):
+    """Sequence lengths around the 8-step checkpoint block and its halves."""
+    inp, gr = _case(2, L, 70, 16, "f32", 1200 + L)
+    _compare(_gpu(inp, gr), _ref(inp, gr), F32_GATE, label="L=%d" % L)
+
+
+def test_bwd_optional_inputs_absent(lib):
+    inp, gr = _case(3, 29, 64, 16, "f32", 1300, h0=False)
+    g = _gpu(inp, gr, use_D=False, use_z=False, use_h0=False, use_dhl=False)
+    assert "dD" not in g and "dz" not in g
+    _compare(g, _ref(inp, gr, use_D=False, use_z=False, use_h0=False, use_dhl=False), F32_GATE, label="absent")
+    g = _gpu(inp, gr, want_dh0=False)
+    assert "dh0" not in g
+    _compare(g, _ref(inp, gr, use_h0=False), F32_GATE, label="no dh0")
+
+
+def test_bwd_long_sequence(lib):
+    """Many blocks: the adjoint runs back through 1000 steps."""
+    inp, gr = _case(1, 1000, 96, 16, "f32", 1400)
+    _compare(_gpu(inp, gr), _ref(inp, gr), F32_GATE, label="L=1000")
+
+
+def test_bwd_deterministic(lib):
+    """Sums are taken in a fixed order: two calls agree bit for bit."""
+    inp, gr = _case(2, 50, 200, 16, "bf16", 1500)
+    a, b = _gpu(inp, gr), _gpu(inp, gr)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_bwd_empty(lib):
+    import torch
+    from selective_state_space_84_amd import binding
+    dev = "cuda:0"
+    A = -torch.arange(1, 17, dtype=torch.float32, device=dev).repeat(8, 1)
+    D = torch.ones(8, device=dev)
+    # seqlen 0: no step uses A or D; the state gradient passes through.
+    x = torch.empty((2, 0, 8), dtype=torch.bfloat16, device=dev)
+    B = torch.empty((2, 0, 16), dtype=torch.bfloat16, device=dev)
+    dhl = torch.randn((2, 8, 16), device=dev)
+    g = binding.ssm_scan_bwd(x, x, A, B, B, D, x, None, dy=x, dh_last=dhl)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(g["dA"]) == 0 and torch.count_nonzero(g["dD"]) == 0
+    assert torch.equal(g["dh0"], dhl)
+    # batch 0: parameter gradients are zero.
+    x = torch.empty((0, 5, 8), dtype=torch.bfloat16, device=dev)
+    B = torch.empty((0, 5, 16), dtype=torch.bfloat16, device=dev)
+    g = binding.ssm_scan_bwd(x, x, A, B, B, D, dy=x)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(g["dA"]) == 0 and torch.count_nonzero(g["dD"]) == 0
+    # d_inner 0: nothing to do.
+    x = torch.empty((2, 5, 0), dtype=torch.bfloat16, device=dev)
+    B = torch.randn((2, 5, 16), device=dev).to(torch.bfloat16)
+    g = binding.ssm_scan_bwd(x, x, A[:0], B, B, dy=x)
+    torch.cuda.synchronize()
+
+
+def _oracle_row(inp, gr, b, threads=16, slice_w=256):
+    """Oracle gradients for all channels of batch row b, in channel slices on
+    threads (the C oracle releases the GIL); dB/dC are summed over slices."""
+    d_inner = inp["x"].shape[2]
+    sl = [(d0, min(d_inner, d0 + slice_w)) for d0 in range(0, d_inner, slice_w)]
+
+    def run(r):
+        d0, d1 = r
+        c = lambda k: inp[k][b:b + 1, :, d0:d1]
+        return oracle.scan_bwd(c("x"), c("delta"), inp["A"][d0:d1], inp["B"][b:b + 1], inp["C"][b:b + 1],
+                               inp["D"][d0:d1], c("z"), None if inp.get("h0") is None else inp["h0"][b:b + 1, d0:d1],
+                               dy=gr["dy"][b:b + 1, :, d0:d1], dh_last=gr["dh_last"][b:b + 1, d0:d1])
+
+    with ThreadPoolExecutor(min(threads, os.cpu_count() or 1)) as ex:
+        parts = list(ex.map(run, sl))
+    out = {k: np.concatenate([p[k] for p in parts], axis=2) for k in ("dx", "ddelta", "dz")}
+    out["dh0"] = np.concatenate([p["dh0"] for p in parts], axis=1)
+    out["dB"] = sum(p["dB"] for p in parts)
+    out["dC"] = sum(p["dC"] for p in parts)
+    return out
+
+
+def test_bwd_full_size_mamba_1p4b(lib):
+    """The full 32 x 4096 x 4096 x 16 bf16 layer in the launch configuration
+    the benchmark times: one whole batch row (every channel, so its dB and dC
+    are complete sums) and dA, dD for sampled channels (summed over all 32
+    rows) against the oracle."""
+    import torch
+    from gpu_util import to_dev, to_host_f64
+    from selective_state_space_84_amd import binding
+    cfg = inputs.MAMBA_1P4B
+    print("generating", cfg.name, flush=True)
+    inp = inputs.scan_inputs(cfg)
+    gr = inputs.make_scan_grads(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, cfg.seed)
+    d = {k: to_dev(inp.get(k)) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0")}
+    print("launching", flush=True)
+    g = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
+                             dy=to_dev(gr["dy"]), dh_last=to_dev(gr["dh_last"]))
+    torch.cuda.synchronize()
+    b = cfg.batch - 1
+    row = {k: to_host_f64(g[k][b:b + 1]) for k in ("dx", "ddelta", "dz", "dh0", "dB", "dC")}
+    print("oracle row", b, flush=True)
+    ref = _oracle_row(inp, gr, b)
+    _compare(row, ref, BF16_GATE, label="1.4b row %d" % b)
+    # dA, dD: sums over every batch row, for sampled channels.
+    rng = np.random.default_rng(7)
+    chans = sorted({0, cfg.d_inner - 1, 63, 64} | set(int(c) for c in rng.integers(0, cfg.d_inner, 12)))
+    dA = to_host_f64(g["dA"])[chans]
+    dD = to_host_f64(g["dD"])[chans]
+
+    def one(bd):
+        bb, dd = bd
+        c = lambda k: inp[k][bb:bb + 1, :, dd:dd + 1]
+        r = oracle.scan_bwd(c("x"), c("delta"), inp["A"][dd:dd + 1], inp["B"][bb:bb + 1], inp["C"][bb:bb + 1],
+                            inp["D"][dd:dd + 1], c("z"), None, dy=gr["dy"][bb:bb + 1, :, dd:dd + 1],
+                            dh_last=gr["dh_last"][bb:bb + 1, dd:dd + 1])
+        return bd, r["dA"][0], r["dD"][0]
+
+    print("oracle dA/dD", len(chans), "channels", flush=True)
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        res = list(ex.map(one, [(bb, dd) for dd in chans for bb in range(cfg.batch)]))
+    rA = np.zeros((len(chans), cfg.d_state))
+    rD = np.zeros(len(chans))
+    for (bb, dd), a, dv in res:
+        rA[chans.index(dd)] += a
+        rD[chans.index(dd)] += dv
+    _compare({"dA": dA, "dD": dD}, {"dA": rA, "dD": rD}, F32_GATE, label="1.4b dA/dD")
