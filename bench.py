@@ -190,6 +190,40 @@ def bench_conv(cfg, steps, dev, d_conv=4):
             "frac_of_8tbs": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "input_gen_s": round(gen_s, 1)}
 
 
+def bench_bwd(cfg, inp, steps, dev):
+    """Gradient of the scan (ssm_scan_bwd) on the scan workload, with
+    seeded upstream gradients dy (io type) and dh_last."""
+    import torch
+    from selective_state_space_84_amd import binding, inputs
+    gr = inputs.make_scan_grads(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, 200 + cfg.seed)
+    d = {k: to_dev(inp.get(k), dev) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0")}
+    dy, dhl = to_dev(gr["dy"], dev), to_dev(gr["dh_last"], dev)
+    ws = torch.empty(binding.scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state),
+                     dtype=torch.uint8, device=dev)
+    grads = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], dy=dy,
+                                 dh_last=dhl, workspace=ws)
+
+    def step():
+        binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], dy=dy,
+                             dh_last=dhl, workspace=ws, grads=grads)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    el = cfg.batch * cfg.seqlen * cfg.d_inner
+    return {"workload": cfg.name + " scan backward (all gradients)", "steps": steps, "ms_per_step": round(ms, 6),
+            "elements_per_s": round(el / (ms * 1e-3), 1),
+            "workspace_bytes": int(ws.numel())}
+
+
 def cpu_baseline(cfg, inp, y_dev, hl_dev, budget_s=12.0, flags=0):
     """fp64 oracle (single thread) on whole batch rows of the same workload,
     row after row until the time budget is spent; also compares those rows'
@@ -243,6 +277,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--n-split", type=int, default=0, help="override the launch plan (tuning)")
     ap.add_argument("--chunk-len", type=int, default=0, help="override the launch plan (tuning)")
@@ -307,6 +342,9 @@ def main():
         out["parity"] = par
     del y, hl
     torch.cuda.empty_cache()
+    if not args.no_bwd and not flags and cfg.d_state <= 16:
+        out["scan_bwd"] = bench_bwd(cfg, inp, max(1, args.steps // 2), dev)
+        torch.cuda.empty_cache()
     if not args.no_conv:
         out["conv1d"] = bench_conv(cfg, args.steps, dev)
         torch.cuda.empty_cache()

@@ -111,6 +111,13 @@ const char* ssm_strerror(int status);
  *               rounding.
  *   flags     : SSM_FLAG_* bits.
  *   dt_bias   : [d_inner] fp32, required with SSM_FLAG_DELTA_SOFTPLUS, else ignored.
+ *   ckpt_out  : NULL, or a buffer of ssm_scan_ckpt_bytes() bytes (4-byte
+ *               aligned, overlapping no other argument) that receives the
+ *               state before every block of 8 steps: what ssm_scan_bwd needs
+ *               to skip recomputing it (training keeps a few states and
+ *               recomputes the rest, "SSMs for long-document QA"
+ *               (pwwt.cn/news/5168881) section 3.2).  An explicit chunk_len
+ *               must then be a multiple of 8 (else SSM_ERR_UNSUPPORTED).
  */
 typedef struct ssm_scan_opts {
   int32_t n_split;
@@ -119,7 +126,15 @@ typedef struct ssm_scan_opts {
   uint32_t flags;
   uint32_t reserved1;
   const float* dt_bias;
+  float* ckpt_out;
 } ssm_scan_opts_t;
+
+/*
+ * Bytes of the state checkpoints the forward scan can save for the backward
+ * pass: [batch][ceil(seqlen/8)][d_state][d_inner] fp32, the state before
+ * every block of 8 steps.  Returns (size_t)-1 for invalid sizes.
+ */
+size_t ssm_scan_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state);
 
 /*
  * Workspace bytes ssm_scan_fwd needs for these sizes (0 when the sequence is
@@ -219,6 +234,9 @@ size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inne
  *   x, delta, A, B, C, D, z, h0, dt_bias : as for ssm_scan_fwd_ex.
  *   dy          : [batch][seqlen][d_inner] io_dtype, gradient of y.
  *   dh_last     : [batch][d_inner][d_state] fp32 gradient of h_last, or NULL for 0.
+ *   ckpt        : NULL, or the checkpoints the forward call wrote through
+ *                 ssm_scan_opts_t.ckpt_out (same inputs): the backward pass
+ *                 then skips its own forward sweep.
  *   dx, ddelta  : [batch][seqlen][d_inner] io_dtype.  ddelta is taken with
  *                 respect to the delta argument as passed: the raw projection
  *                 when SSM_FLAG_DELTA_SOFTPLUS is set.
@@ -244,7 +262,7 @@ size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inne
  */
 int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const void* z, const float* h0, const float* dt_bias, const void* dy, const float* dh_last,
-                 void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* dh0,
+                 const float* ckpt, void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* dh0,
                  float* d_dt_bias, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                  int32_t io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream);
 

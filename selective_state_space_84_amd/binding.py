@@ -40,7 +40,8 @@ _SZ = ctypes.c_size_t
 class ScanOpts(ctypes.Structure):
     """Mirror of ssm_scan_opts_t."""
     _fields_ = [("n_split", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("chunk_len", ctypes.c_int64),
-                ("flags", ctypes.c_uint32), ("reserved1", ctypes.c_uint32), ("dt_bias", ctypes.c_void_p)]
+                ("flags", ctypes.c_uint32), ("reserved1", ctypes.c_uint32), ("dt_bias", ctypes.c_void_p),
+                ("ckpt_out", ctypes.c_void_p)]
 
 
 SIGNATURES = {
@@ -55,7 +56,8 @@ SIGNATURES = {
     "ssm_state_update": ([_P] * 9 + [_I64] * 3 + [_I32, _P], ctypes.c_int),
     "ssm_state_update_ex": ([_P] * 9 + [_I64] * 3 + [_I32, _U32, _P, _P], ctypes.c_int),
     "ssm_scan_bwd_workspace_size": ([_I64, _I64, _I64, _I64], _SZ),
-    "ssm_scan_bwd": ([_P] * 20 + [_I64] * 4 + [_I32, _U32, _P, _SZ, _P], ctypes.c_int),
+    "ssm_scan_ckpt_bytes": ([_I64, _I64, _I64, _I64], _SZ),
+    "ssm_scan_bwd": ([_P] * 21 + [_I64] * 4 + [_I32, _U32, _P, _SZ, _P], ctypes.c_int),
     "ssm_conv1d_fwd": ([_P] * 6 + [_I64] * 4 + [_I32, _I32, _P], ctypes.c_int),
     "ssm_conv1d_update": ([_P] * 5 + [_I64] * 3 + [_I32, _I32, _P], ctypes.c_int),
 }
@@ -95,8 +97,16 @@ def strerror(status: int) -> str:
     return load_library().ssm_strerror(status).decode()
 
 
-def _opts(n_split=0, chunk_len=0, flags=0, dt_bias=None) -> ScanOpts:
-    return ScanOpts(n_split, 0, chunk_len, flags, 0, _ptr(dt_bias))
+def _opts(n_split=0, chunk_len=0, flags=0, dt_bias=None, ckpt_out=None) -> ScanOpts:
+    return ScanOpts(n_split, 0, chunk_len, flags, 0, _ptr(dt_bias), _ptr(ckpt_out))
+
+
+def scan_ckpt_bytes(batch, seqlen, d_inner, d_state) -> int:
+    """Bytes of the block-start state checkpoints a forward call can save."""
+    n = load_library().ssm_scan_ckpt_bytes(batch, seqlen, d_inner, d_state)
+    if n == ctypes.c_size_t(-1).value:
+        raise SsmError(SSM_ERR_BAD_DIM, "ssm_scan_ckpt_bytes")
+    return n
 
 
 def _ptr(t) -> Optional[int]:
@@ -151,12 +161,14 @@ def scan_workspace_size(batch, seqlen, d_inner, d_state, n_split=0, chunk_len=0,
 
 
 def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, y=None, h_last=None, want_h_last=True,
-                 workspace=None, n_split=0, chunk_len=0, flags=0, dt_bias=None, stream=None):
+                 workspace=None, n_split=0, chunk_len=0, flags=0, dt_bias=None, ckpt_out=None, stream=None):
     """Selective scan over the sequence; returns (y, h_last).
 
     x, delta, z: (batch, seqlen, d_inner); A: (d_inner, d_state) fp32;
     B, C: (batch, seqlen, d_state); D: (d_inner,) fp32; h0: (batch, d_inner, d_state) fp32.
     io tensors are all bfloat16 or all float32.  Outputs are allocated when not given.
+    ckpt_out: optional fp32 buffer of scan_ckpt_bytes() bytes that receives the
+    state before every 8-step block (for ssm_scan_bwd(ckpt=...)).
     """
     import torch
     batch, seqlen, d_inner = x.shape
@@ -170,7 +182,7 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, y=None, h_last=N
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    o = _opts(n_split, chunk_len, flags, dt_bias)
+    o = _opts(n_split, chunk_len, flags, dt_bias, ckpt_out)
     rc = load_library().ssm_scan_fwd_ex(
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
         batch, seqlen, d_inner, d_state, dt, ctypes.byref(o), _ptr(workspace), ws_have, _stream(stream))
@@ -203,8 +215,10 @@ def scan_bwd_workspace_size(batch, seqlen, d_inner, d_state) -> int:
 
 
 def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, flags=0, dt_bias=None,
-                 want_dh0=True, grads=None, workspace=None, stream=None):
+                 ckpt=None, want_dh0=True, grads=None, workspace=None, stream=None):
     """Gradient of ssm_scan_fwd for L = sum(dy * y) + sum(dh_last * h_last).
+
+    ckpt: optional checkpoints saved by the forward call (ssm_scan_fwd(ckpt_out=...)).
 
     Returns a dict with dx, ddelta (w.r.t. the delta argument as passed), dA,
     dB, dC (fp32), and dD, dz, dh0, d_dt_bias when D, z, want_dh0, the softplus
@@ -241,7 +255,7 @@ def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load_library().ssm_scan_bwd(
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dt_bias), _ptr(dy),
-        _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+        _ptr(dh_last), _ptr(ckpt), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
         _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("dh0")), _ptr(g.get("d_dt_bias")), batch, seqlen, d_inner,
         d_state, dt, flags, _ptr(workspace), ws_have, _stream(stream))
     if rc != SSM_OK:

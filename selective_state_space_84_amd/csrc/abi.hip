@@ -130,7 +130,9 @@ int scan_impl(const void* x, const void* delta, const float* A, const void* B, c
   if (!scan_d_state_ok(d_state)) return SSM_ERR_UNSUPPORTED;
   const uint32_t flags = opts != nullptr ? opts->flags : 0u;
   const float* dt_bias = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? opts->dt_bias : nullptr;
+  float* ckpt = opts != nullptr ? opts->ckpt_out : nullptr;
   if (flags & ~kKnownFlags) return SSM_ERR_UNSUPPORTED;
+  if (ckpt != nullptr && opts->chunk_len > 0 && opts->chunk_len % ssm::kTimeBlock != 0) return SSM_ERR_UNSUPPORTED;
   const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
 
   int64_t n_io, n_bc, n_h, n_a;
@@ -155,7 +157,24 @@ int scan_impl(const void* x, const void* delta, const float* A, const void* B, c
       !aligned(dt_bias, 4))
     return SSM_ERR_MISALIGNED;
 
-  // Aliasing: y overlaps nothing; h_last overlaps nothing except h0 exactly.
+  if (!aligned(ckpt, 4)) return SSM_ERR_MISALIGNED;
+  int64_t b_ck = 0;
+  if (ckpt != nullptr) {
+    int64_t n_ck;
+    if (!mul3(batch, (seqlen + ssm::kTimeBlock - 1) / ssm::kTimeBlock, d_state, &n_ck) ||
+        __builtin_mul_overflow(n_ck, d_inner * 4, &b_ck))
+      return SSM_ERR_BAD_DIM;
+  }
+
+  // Aliasing: y overlaps nothing; h_last overlaps nothing except h0 exactly;
+  // the checkpoints overlap nothing.
+  {
+    const void* all[] = {x, delta, z, B, C, A, D, h0, y, h_last, dt_bias};
+    const int64_t allb[] = {b_io, b_io, z ? b_io : 0, b_bc, b_bc, b_a, D ? b_d : 0, h0 ? b_h : 0, b_io,
+                            h_last ? b_h : 0, dt_bias ? b_d : 0};
+    for (int k = 0; k < 11; ++k)
+      if (overlap(ckpt, b_ck, all[k], allb[k])) return SSM_ERR_ALIAS;
+  }
   const void* ins[] = {x, delta, z, B, C, A, D, h0};
   const int64_t inb[] = {b_io, b_io, z ? b_io : 0, b_bc, b_bc, b_a, D ? b_d : 0, h0 ? b_h : 0};
   for (int k = 0; k < 8; ++k)
@@ -186,6 +205,7 @@ int scan_impl(const void* x, const void* delta, const float* A, const void* B, c
                             h_last ? b_h : 0, dt_bias ? b_d : 0};
     for (int k = 0; k < 11; ++k)
       if (overlap(workspace, (int64_t)need, all[k], allb[k])) return SSM_ERR_ALIAS;
+    if (overlap(workspace, (int64_t)need, ckpt, b_ck)) return SSM_ERR_ALIAS;
   }
   int64_t state_blocks = (n_h + 255) / 256;
   if (state_blocks > INT32_MAX) return SSM_ERR_BAD_DIM;
@@ -196,7 +216,7 @@ int scan_impl(const void* x, const void* delta, const float* A, const void* B, c
     if (h_last == nullptr || h_last == h0) return SSM_OK;
     return ssm::launch_state_fill(h_last, h0, n_h, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
-  ssm::ScanLaunch p{x, delta, A, B, C, D, z, h0, y, h_last, static_cast<float*>(workspace), dt_bias, flags, batch,
+  ssm::ScanLaunch p{x, delta, A, B, C, D, z, h0, y, h_last, static_cast<float*>(workspace), ckpt, dt_bias, flags, batch,
                     seqlen, d_inner, (int32_t)d_state, pl.n_split, pl.chunk_len, pl.n_chunks,
                     io_dtype == SSM_DTYPE_BF16, s};
   return ssm::launch_scan(p) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
@@ -263,7 +283,8 @@ int64_t bwd_workspace_floats(int64_t batch, int64_t seqlen, int64_t d_inner, int
 }
 
 int bwd_impl(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-             const void* z, const float* h0, const float* dt_bias, const void* dy, const float* dh_last, void* dx,
+             const void* z, const float* h0, const float* dt_bias, const void* dy, const float* dh_last,
+             const float* ckpt, void* dx,
              void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* dh0, float* d_dt_bias,
              int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int32_t io_dtype, uint32_t flags,
              void* workspace, size_t workspace_bytes, void* stream) {
@@ -303,19 +324,26 @@ int bwd_impl(const void* x, const void* delta, const float* A, const void* B, co
   if (!aligned(x, es) || !aligned(delta, es) || !aligned(z, es) || !aligned(dy, es) || !aligned(dx, es) ||
       !aligned(ddelta, es) || !aligned(dz, es))
     return SSM_ERR_MISALIGNED;
-  const void* f4[] = {A, B, C, D, h0, dt_bias, dh_last, dA, dB, dC, dD, dh0, d_dt_bias};
+  const void* f4[] = {A, B, C, D, h0, dt_bias, dh_last, ckpt, dA, dB, dC, dD, dh0, d_dt_bias};
   for (const void* q : f4)
     if (!aligned(q, 4)) return SSM_ERR_MISALIGNED;
 
   // Aliasing: no output overlaps an input, another output or the workspace.
-  const void* ins[] = {x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last};
+  int64_t b_ck = 0;
+  if (ckpt != nullptr) {
+    int64_t n_ck;
+    if (!mul3(batch, (seqlen + ssm::kBwdBlock - 1) / ssm::kBwdBlock, d_state, &n_ck) ||
+        __builtin_mul_overflow(n_ck, d_inner * 4, &b_ck))
+      return SSM_ERR_BAD_DIM;
+  }
+  const void* ins[] = {x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, ckpt};
   const int64_t inb[] = {b_io, b_io, b_a, b_bc, b_bc, D ? b_d : 0, z ? b_io : 0, h0 ? b_h : 0,
-                         dt_bias ? b_d : 0, b_io, dh_last ? b_h : 0};
+                         dt_bias ? b_d : 0, b_io, dh_last ? b_h : 0, b_ck};
   const void* outs[] = {dx, ddelta, dA, dB, dC, dD, dz, dh0, d_dt_bias};
   const int64_t outb[] = {b_io, b_io, b_a, b_bc32, b_bc32, dD ? b_d : 0, dz ? b_io : 0, dh0 ? b_h : 0,
                           d_dt_bias ? b_d : 0};
   for (int o = 0; o < 9; ++o) {
-    for (int k = 0; k < 11; ++k)
+    for (int k = 0; k < 12; ++k)
       if (overlap(outs[o], outb[o], ins[k], inb[k])) return SSM_ERR_ALIAS;
     for (int k = o + 1; k < 9; ++k)
       if (overlap(outs[o], outb[o], outs[k], outb[k])) return SSM_ERR_ALIAS;
@@ -327,7 +355,7 @@ int bwd_impl(const void* x, const void* delta, const float* A, const void* B, co
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < (size_t)need) return SSM_ERR_WORKSPACE;
     if (!aligned(workspace, kWorkspaceAlign)) return SSM_ERR_MISALIGNED;
-    for (int k = 0; k < 11; ++k)
+    for (int k = 0; k < 12; ++k)
       if (overlap(workspace, need, ins[k], inb[k])) return SSM_ERR_ALIAS;
     for (int k = 0; k < 9; ++k)
       if (overlap(workspace, need, outs[k], outb[k])) return SSM_ERR_ALIAS;
@@ -339,7 +367,7 @@ int bwd_impl(const void* x, const void* delta, const float* A, const void* B, co
   if (d_inner == 0) return SSM_OK;
   float* ws = static_cast<float*>(workspace);
   const ssm::BwdWorkspace lay = ssm::bwd_workspace_layout(ws, batch, seqlen, d_inner, d_state, nullptr);
-  ssm::BwdLaunch p{x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0,
+  ssm::BwdLaunch p{x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, ckpt, dx, ddelta, dA, dB, dC, dD, dz, dh0,
                    d_dt_bias, flags, batch, seqlen, d_inner, (int32_t)d_state, io_dtype == SSM_DTYPE_BF16,
                    static_cast<hipStream_t>(stream)};
   return ssm::launch_scan_bwd(p, lay) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
@@ -410,12 +438,21 @@ size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inne
   return (size_t)floats * 4;
 }
 
+size_t ssm_scan_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  if (check_dims(batch, seqlen, d_inner, d_state) != SSM_OK) return (size_t)-1;
+  int64_t n, bytes;
+  if (!mul3(batch, (seqlen + ssm::kTimeBlock - 1) / ssm::kTimeBlock, d_state, &n) ||
+      __builtin_mul_overflow(n, d_inner * 4, &bytes))
+    return (size_t)-1;
+  return (size_t)bytes;
+}
+
 int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const void* z, const float* h0, const float* dt_bias, const void* dy, const float* dh_last,
-                 void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* dh0,
-                 float* d_dt_bias, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                 const float* ckpt, void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
+                 float* dh0, float* d_dt_bias, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                  int32_t io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, d_dt_bias,
+  return bwd_impl(x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, ckpt, dx, ddelta, dA, dB, dC, dD, dz, dh0, d_dt_bias,
                   batch, seqlen, d_inner, d_state, io_dtype, flags, workspace, workspace_bytes, stream);
 }
 

@@ -76,13 +76,19 @@ __device__ __forceinline__ float gld(const gchar* base, uint32_t off) {
   return io_to_f32(*reinterpret_cast<const T __attribute__((address_space(1)))*>(base + off));
 }
 template <typename T>
+__device__ __forceinline__ T gldr(const gchar* base, uint32_t off) {
+  return *reinterpret_cast<const T __attribute__((address_space(1)))*>(base + off);
+}
+template <typename T>
 __device__ __forceinline__ void gst(gchar* base, uint32_t off, float v) {
   T bits;
   io_store(&bits, v);
   *reinterpret_cast<T __attribute__((address_space(1)))*>(base + off) = bits;
 }
 
-// ckpt[b][k][n][d] = state before step k * kBB, k = 0 .. nblk-1.
+// ckpt[b][k][n][d] = state before step k * kBB, k = 0 .. nblk-1 (used when
+// the forward call did not save them).  B rows arrive one step ahead
+// through SGPRs; x and delta one block ahead.
 template <typename T, int N, int MODE>
 __global__ void __launch_bounds__(64)
     k_bwd_ckpt(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
@@ -96,6 +102,8 @@ __global__ void __launch_bounds__(64)
   const int64_t d = (int64_t)tile * 64 + lane;
   const bool dvalid = d < DI;
   const int64_t dc = dvalid ? d : DI - 1;
+  const int64_t cbase = (int64_t)tile * 64;
+  const int lc = (int)(dc - cbase);
 
   float Al2[N], h[N];
 #pragma unroll
@@ -104,23 +112,35 @@ __global__ void __launch_bounds__(64)
     h[n] = h0 != nullptr ? h0[(b * DI + dc) * N + n] : 0.f;
   }
   const float dtb = (MODE & 1) ? dt_bias[dc] : 0.f;
-  const T* xc = x + b * L * DI + dc;
-  const T* dlc = delta + b * L * DI + dc;
+  const uint32_t row_bytes = (uint32_t)(DI * (int64_t)sizeof(T));
+  uint32_t voff[kBB];
+#pragma unroll
+  for (int i = 0; i < kBB; ++i) voff[i] = (uint32_t)lc * (uint32_t)sizeof(T) + (uint32_t)i * row_bytes;
+  auto rowp = [&](const void* base, int64_t t) {
+    return uniform_ptr(reinterpret_cast<const char*>(base) + ((b * L + t) * DI + cbase) * (int64_t)sizeof(T));
+  };
   const T* Bb = B + b * L * N;
   float* cp = ckpt + b * dm.nblk * N * DI + d;
 
   // Only blocks 0 .. nblk-2 are stepped through (the state after the last
   // block is not needed), and all of them are full.
+  // Raw values: widening happens at use, so the next block's loads stay in
+  // flight while this block computes.
   T xn[kBB], dn[kBB];
   auto fetch = [&](int k) {
+    const gchar* xb = rowp(x, (int64_t)k * kBB);
+    const gchar* db = rowp(delta, (int64_t)k * kBB);
 #pragma unroll
     for (int i = 0; i < kBB; ++i) {
-      const int64_t o = ((int64_t)k * kBB + i) * DI;
-      xn[i] = xc[o];
-      dn[i] = dlc[o];
+      xn[i] = gldr<T>(xb, voff[i]);
+      dn[i] = gldr<T>(db, voff[i]);
     }
   };
-  if (dm.nblk > 1) fetch(0);
+  StateRow<T, N> bq;
+  if (dm.nblk > 1) {
+    fetch(0);
+    bq.load(Bb);
+  }
   for (int k = 0; k < dm.nblk; ++k) {
     if (dvalid) {
 #pragma unroll
@@ -134,11 +154,14 @@ __global__ void __launch_bounds__(64)
       dr[i] = dn[i];
     }
     if (k + 2 < dm.nblk) fetch(k + 1);
-    const T* Bk = Bb + (int64_t)k * kBB * N;
 #pragma unroll
     for (int i = 0; i < kBB; ++i) {
-      StateRow<T, N> br;
-      br.load(Bk + i * N);
+      bq.touch();
+      __builtin_amdgcn_sched_barrier(0);
+      const StateRow<T, N> br = bq;
+      // The next row is at most (nblk - 1) * kBB < seqlen.
+      bq.load(Bb + ((int64_t)k * kBB + i + 1) * N);
+      __builtin_amdgcn_sched_barrier(0);
       float dt = io_to_f32(dr[i]);
       if (MODE & 1) dt = softplus(dt + dtb);
       const float wx = dt * io_to_f32(xr[i]);
@@ -146,6 +169,7 @@ __global__ void __launch_bounds__(64)
       for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(hw_exp2(dt * Al2[n]), h[n], wx * br.get(n));
     }
   }
+  if (dm.nblk > 1) bq.touch();
 }
 
 // Steps of abar * h_{t-1} a lane keeps in VGPRs at once.  With 16 states a
@@ -503,13 +527,15 @@ hipError_t launch_bwd_t(const BwdLaunch& p, const BwdWorkspace& ws) {
   hipError_t e;
   const unsigned waves = (unsigned)(p.batch * tiles);
   if (waves > 0) {
-    if (dm.nblk > 0) {
+    const float* ck = p.ckpt;
+    if (ck == nullptr && dm.nblk > 0) {
       e = launch(k_bwd_ckpt<T, N, MODE>, dim3(waves), dim3(64), 0, p.stream, x, dl, p.A, Bm, p.h0, p.dt_bias,
                  ws.ckpt, dm);
       if (e != hipSuccess) return e;
+      ck = ws.ckpt;
     }
     e = launch(k_bwd_sweep<T, N, MODE>, dim3(waves), dim3(64), 0, p.stream, x, dl, p.A, Bm, Cm, p.D,
-               static_cast<const T*>(p.z), static_cast<const T*>(p.dy), p.dh_last, p.dt_bias, ws.ckpt,
+               static_cast<const T*>(p.z), static_cast<const T*>(p.dy), p.dh_last, p.dt_bias, ck,
                static_cast<T*>(p.dx), static_cast<T*>(p.ddelta), static_cast<T*>(p.dz), p.dh0, ws.part_bc,
                ws.part_a, ws.part_d, ws.part_t, dm);
     if (e != hipSuccess) return e;

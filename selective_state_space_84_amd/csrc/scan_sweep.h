@@ -79,6 +79,7 @@ struct SweepDims {
   int32_t tiles, n_chunks_grid;  // chunks covered by this launch
   int32_t n_chunks;              // chunks of the whole sequence
   int32_t h_init_chunked;        // h_init is [n_chunks][B][d][N] (else [B][d][N])
+  float* ckpt;                   // nullable: state at every kTB-step block start, [B][ceil(L/kTB)][N][d]
 };
 
 // One sweep over a (batch row, chunk, 64-channel tile).  N = d_state, NS =
@@ -208,9 +209,23 @@ __global__ void __launch_bounds__(64 * (N / NS))
 
   // One block of kTB steps starting at tb.  FULL: no clamping anywhere
   // (callers guarantee tb + 2 * kTB <= nsteps).
+  // Checkpoints for the backward pass: the state before every block of kTB
+  // steps (chunks start on block boundaries when this is requested).
+  float* ck = (!SUMMARY && dm.ckpt != nullptr)
+                  ? dm.ckpt + ((b * ((dm.seqlen + kTB - 1) / kTB) + t_beg / kTB) * N + n0) * DI + d
+                  : nullptr;
+  const int64_t ck_step = (int64_t)N * DI;  // floats between consecutive blocks
+
   auto block = [&](int tb, auto full_t) {
     constexpr bool kFull = decltype(full_t)::value;
     const int nt = kFull ? kTB : min(kTB, nsteps - tb);
+    if (!SUMMARY && ck != nullptr) {
+      if (dvalid) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) ck[(int64_t)n * DI] = h[n];
+      }
+      ck += ck_step;
+    }
     T xr[kTB], dr[kTB], zr[kTB];
 #pragma unroll
     for (int i = 0; i < kTB; ++i) {
@@ -356,7 +371,7 @@ hipError_t launch_scan_t(const ScanLaunch& p) {
   const int64_t tiles = (p.d_inner + 63) / 64;
   const int64_t states = p.batch * p.d_inner * N;
   const size_t shmem = G > 1 ? (size_t)2 * G * kTB * 64 * sizeof(float) : 0;
-  SweepDims dm{p.batch, p.seqlen, p.d_inner, p.chunk_len, (int32_t)tiles, 1, (int32_t)p.n_chunks, 0};
+  SweepDims dm{p.batch, p.seqlen, p.d_inner, p.chunk_len, (int32_t)tiles, 1, (int32_t)p.n_chunks, 0, p.ckpt};
   const T* x = static_cast<const T*>(p.x);
   const T* dl = static_cast<const T*>(p.delta);
   const T* Bm = static_cast<const T*>(p.B);

@@ -28,6 +28,7 @@ struct ScanLaunch {
   void* y;
   float* h_last;       // nullable
   float* workspace;    // nullable when n_chunks == 1
+  float* ckpt;         // nullable: states at 8-step block starts for the backward pass
   const float* dt_bias;  // [d_inner], used with SSM_FLAG_DELTA_SOFTPLUS
   uint32_t flags;        // SSM_FLAG_* (bit 0 softplus step, bit 1 exact ZOH)
   int64_t batch, seqlen, d_inner;
@@ -95,6 +96,7 @@ struct BwdLaunch {
   const float* dt_bias;  // used with SSM_FLAG_DELTA_SOFTPLUS
   const void* dy;
   const float* dh_last;  // nullable
+  const float* ckpt;     // nullable: block-start states written by the forward sweep
   void* dx;
   void* ddelta;
   float* dA;

@@ -65,6 +65,14 @@ def test_scan_argument_errors(lib):
     assert _scan(lib, y=P0 + 16) == bd.SSM_ERR_ALIAS
     assert _scan(lib, h_last=P0 + 64) == bd.SSM_ERR_ALIAS
     assert _scan(lib, h0=P0 + 9 * MB, h_last=P0 + 9 * MB + 64) == bd.SSM_ERR_ALIAS
+    # Checkpoint output: size query, alignment, aliasing, chunks on 8-step boundaries.
+    assert lib.ssm_scan_ckpt_bytes(2, 4, 8, 16) == 2 * 1 * 16 * 8 * 4
+    assert lib.ssm_scan_ckpt_bytes(3, 17, 5, 4) == 3 * 3 * 4 * 5 * 4
+    assert lib.ssm_scan_ckpt_bytes(-1, 4, 8, 16) == ctypes.c_size_t(-1).value
+    ck = P0 + 40 * MB
+    assert _scan(lib, opts=bd.ScanOpts(0, 0, 0, 0, 0, None, ck + 2)) == bd.SSM_ERR_MISALIGNED
+    assert _scan(lib, opts=bd.ScanOpts(0, 0, 0, 0, 0, None, P0 + 8 * MB)) == bd.SSM_ERR_ALIAS
+    assert _scan(lib, opts=bd.ScanOpts(0, 0, 12, 0, 0, None, ck)) == bd.SSM_ERR_UNSUPPORTED
     # Unsupported flags and tuning options.
     assert _scan(lib, opts=bd.ScanOpts(0, 0, 0, 0x80, 0, None)) == bd.SSM_ERR_UNSUPPORTED
     # The softplus step needs dt_bias: present, 4-byte aligned, not overlapping outputs.
@@ -163,14 +171,14 @@ def test_conv_argument_errors(lib):
 
 
 def _bwd(lib, x=P0, delta=P0 + MB, A=P0 + 2 * MB, B=P0 + 3 * MB, C=P0 + 4 * MB, D=None, z=None, h0=None,
-         dt_bias=None, dy=P0 + 5 * MB, dh_last=None, dx=P0 + 10 * MB, ddelta=P0 + 11 * MB, dA=P0 + 12 * MB,
+         dt_bias=None, dy=P0 + 5 * MB, dh_last=None, ckpt=None, dx=P0 + 10 * MB, ddelta=P0 + 11 * MB, dA=P0 + 12 * MB,
          dB=P0 + 13 * MB, dC=P0 + 14 * MB, dD=None, dz=None, dh0=None, d_dt_bias=None, batch=2, L=4, d=8, N=16,
          dtype=1, flags=0, ws=P0 + 64 * MB, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = lib.ssm_scan_bwd_workspace_size(batch, L, d, N) if batch >= 0 and L >= 0 and d >= 0 else 0
         if ws_bytes == ctypes.c_size_t(-1).value:
             ws_bytes = 0
-    return lib.ssm_scan_bwd(x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0,
+    return lib.ssm_scan_bwd(x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, ckpt, dx, ddelta, dA, dB, dC, dD, dz, dh0,
                             d_dt_bias, batch, L, d, N, dtype, flags, ws, ws_bytes, None)
 
 
@@ -214,6 +222,9 @@ def test_bwd_argument_errors(lib):
     assert _bwd(lib, dx=P0 + 32) == bd.SSM_ERR_ALIAS
     assert _bwd(lib, ddelta=P0 + 10 * MB + 8) == bd.SSM_ERR_ALIAS
     assert _bwd(lib, ws=P0 + 12 * MB) == bd.SSM_ERR_ALIAS
+    # Forward checkpoints given to the backward: aligned, not overlapping an output.
+    assert _bwd(lib, ckpt=P0 + 40 * MB + 2) == bd.SSM_ERR_MISALIGNED
+    assert _bwd(lib, ckpt=P0 + 12 * MB) == bd.SSM_ERR_ALIAS
     # Workspace: missing, too small, misaligned.
     assert _bwd(lib, ws=None) == bd.SSM_ERR_WORKSPACE
     need = lib.ssm_scan_bwd_workspace_size(2, 4, 8, 16)

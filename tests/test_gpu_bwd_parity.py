@@ -141,6 +141,37 @@ def test_bwd_empty(lib):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("chunk_len,n_split", [(0, 1), (64, 1), (0, 2), (24, 4)])
+def test_forward_checkpoints_feed_backward(lib, chunk_len, n_split):
+    """The forward scan's saved block-start states equal the oracle's state
+    before every 8-step block (whole sequence, chunked, states split over
+    waves), and the backward pass fed with them matches the oracle gradient."""
+    import torch
+    from gpu_util import to_dev, to_host_f64
+    from selective_state_space_84_amd import binding
+    batch, L, dI, N = 2, 70, 100, 16
+    inp, gr = _case(batch, L, dI, N, "f32", 1600 + chunk_len + n_split)
+    d = {k: to_dev(inp.get(k)) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0")}
+    nblk = -(-L // 8)
+    ck = torch.full((binding.scan_ckpt_bytes(batch, L, dI, N) // 4,), float("nan"), device="cuda:0")
+    binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], ckpt_out=ck,
+                         chunk_len=chunk_len, n_split=n_split)
+    torch.cuda.synchronize()
+    got = to_host_f64(ck).reshape(batch, nblk, N, dI)
+    for k in range(nblk):
+        if k == 0:
+            ref = inp["h0"].astype(np.float64)
+        else:
+            t = 8 * k
+            _, ref = oracle.scan(inp["x"][:, :t], inp["delta"][:, :t], inp["A"], inp["B"][:, :t], inp["C"][:, :t],
+                                 inp["D"], inp["z"][:, :t], inp["h0"])
+        assert floored_rel_err(got[:, k].transpose(0, 2, 1), ref) <= 1e-5, k
+    g = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
+                             dy=to_dev(gr["dy"]), dh_last=to_dev(gr["dh_last"]), ckpt=ck)
+    torch.cuda.synchronize()
+    _compare({k: to_host_f64(v) for k, v in g.items()}, _ref(inp, gr), F32_GATE, label="ckpt-fed")
+
+
 def _oracle_row(inp, gr, b, threads=16, slice_w=256):
     """Oracle gradients for all channels of batch row b, in channel slices on
     threads (the C oracle releases the GIL); dB/dC are summed over slices."""
@@ -180,6 +211,17 @@ def test_bwd_full_size_mamba_1p4b(lib):
     g = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
                              dy=to_dev(gr["dy"]), dh_last=to_dev(gr["dh_last"]))
     torch.cuda.synchronize()
+    # The forward scan's checkpoints (the training path) give the same gradients.
+    ck = torch.empty((binding.scan_ckpt_bytes(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state) // 4,),
+                     device="cuda:0")
+    binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], ckpt_out=ck)
+    g2 = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
+                              dy=to_dev(gr["dy"]), dh_last=to_dev(gr["dh_last"]), ckpt=ck)
+    torch.cuda.synchronize()
+    for k in g:
+        e = floored_rel_err(to_host_f64(g2[k]), to_host_f64(g[k]))
+        assert e <= 1e-5 if k in ("dA", "dB", "dC", "dD", "dh0") else e <= BF16_GATE, (k, e)
+    del g2, ck
     b = cfg.batch - 1
     row = {k: to_host_f64(g[k][b:b + 1]) for k in ("dx", "ddelta", "dz", "dh0", "dB", "dC")}
     print("oracle row", b, flush=True)
