@@ -5,13 +5,15 @@ One step = one ssm_scan_fwd call over a whole Mamba layer's batch (all of the
 scan's steps: load and unpack, decay, input term, recurrence, readout, gate,
 store, final state), with inputs already resident in HBM.  The default
 workload is the Mamba-1.4B layer shape (batch 32, L 4096, d_inner 4096,
-d_state 16, bf16 io, fp32 state).  The same run also times the decode update
-on its own workload (256 sequences x 5120 channels x 16 states, 1000
-consecutive in-place steps) and the fp64 CPU oracle on a bounded sample of the
-scan workload.  Prints one JSON line.
+d_state 16, bf16 io, fp32 state).  The same run also times, each on its own
+line of the JSON object: the scan's backward pass (standalone, and the
+training path where the forward saves state checkpoints), the causal conv1d
+that feeds the scan, the decode update (256 sequences x 5120 channels x 16
+states, 1000 consecutive in-place steps), and the fp64 CPU oracle on a
+bounded sample of the scan workload.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-decode] [--no-cpu-baseline]
+                       [--no-decode] [--no-conv] [--no-bwd] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -36,9 +38,19 @@ def scan_slots_per_element(d_state: int) -> int:
     return 6 * d_state + 14
 
 
+# Minimum VALU slots per element of the scan's backward pass with the decays
+# computed once: per state and step 7 for the forward recomputation (mul,
+# exp (2), mul, FMA, readout FMA, g*h row), 7 for the adjoint step (FMA, mul,
+# 3 FMA, dB row mul, lam*abar) and 2 for the channel sums of dB and dC; per
+# element ~30 (widening, two sigmoids, dz, dx, ddelta, narrowing).
+def bwd_slots_per_element(d_state: int) -> int:
+    return 16 * d_state + 30
+
+
 def _kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("scan_sweep.h", "scan_mode0.hip", "scan_aux.hip", "update_kernel.hip", "ssm_device.h", "ssm_internal.h"):
+    for f in ("scan_sweep.h", "scan_mode0.hip", "scan_aux.hip", "update_kernel.hip", "conv_kernels.hip",
+              "scan_bwd.hip", "ssm_device.h", "ssm_internal.h"):
         with open(os.path.join(REPO, "selective_state_space_84_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -200,28 +212,46 @@ def bench_bwd(cfg, inp, steps, dev):
     dy, dhl = to_dev(gr["dy"], dev), to_dev(gr["dh_last"], dev)
     ws = torch.empty(binding.scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state),
                      dtype=torch.uint8, device=dev)
+    ck = torch.empty(binding.scan_ckpt_bytes(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state) // 4,
+                     dtype=torch.float32, device=dev)
+    y = torch.empty_like(d["x"])
+    hl = torch.empty((cfg.batch, cfg.d_inner, cfg.d_state), dtype=torch.float32, device=dev)
     grads = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], dy=dy,
                                  dh_last=dhl, workspace=ws)
 
-    def step():
+    def bwd(ckpt=None):
         binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], dy=dy,
-                             dh_last=dhl, workspace=ws, grads=grads)
+                             dh_last=dhl, workspace=ws, grads=grads, ckpt=ckpt)
 
-    for _ in range(2):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    def fwd_ckpt():
+        binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], y=y, h_last=hl,
+                             ckpt_out=ck)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(bwd)
+    ms_fc = timed(fwd_ckpt)
+    ms_bc = timed(lambda: bwd(ck))
     el = cfg.batch * cfg.seqlen * cfg.d_inner
+    slots = bwd_slots_per_element(cfg.d_state)
+    frac = el * slots / (ms_bc * 1e-3) / 1e12 / VALU_PEAK_TSLOTS
     return {"workload": cfg.name + " scan backward (all gradients)", "steps": steps, "ms_per_step": round(ms, 6),
             "elements_per_s": round(el / (ms * 1e-3), 1),
-            "workspace_bytes": int(ws.numel())}
+            "training_path": {"fwd_with_ckpt_ms": round(ms_fc, 6), "bwd_from_ckpt_ms": round(ms_bc, 6),
+                              "fwd_plus_bwd_ms": round(ms_fc + ms_bc, 6)},
+            "alu": {"min_slots_per_element": slots, "frac_of_valu_peak_bwd_from_ckpt": round(frac, 4)},
+            "workspace_bytes": int(ws.numel()), "ckpt_bytes": int(ck.numel() * 4)}
 
 
 def cpu_baseline(cfg, inp, y_dev, hl_dev, budget_s=12.0, flags=0):

@@ -15,10 +15,11 @@ pytestmark = pytest.mark.gpu
 
 SP = 0x1  # SSM_FLAG_DELTA_SOFTPLUS
 
-# Gates on the floored relative error of every gradient (see the design doc for
-# the derivation): fp32 io: long fp32 sums over time, channels and batch rows;
-# bf16 io: dx, ddelta and dz are rounded to bf16 (2^-9 relative).
-F32_GATE = 1e-4
+# Gates on the floored relative error of every gradient.  fp32 io: sized by
+# the float32 emulation in test_tolerance_bwd.py (ddelta's fp32 floor grows
+# with the memory of slow channels: ~6.5e-5 on a 1000-step case); bf16 io:
+# dx, ddelta and dz are rounded to bf16 (2^-9 relative), as for y.
+from test_tolerance_bwd import BWD_F32_GATE as F32_GATE  # noqa: E402
 BF16_GATE = 2e-2
 
 
