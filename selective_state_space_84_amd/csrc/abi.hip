@@ -278,7 +278,7 @@ int64_t bwd_workspace_floats(int64_t batch, int64_t seqlen, int64_t d_inner, int
   if (!mul3(batch, d_inner, d_state, &c)) return -1;
   if (a > INT64_MAX / 8 || b > INT64_MAX / 8 || c > INT64_MAX / 8) return -1;
   int64_t total;
-  ssm::bwd_workspace_layout(nullptr, batch, seqlen, d_inner, d_state, &total);
+  ssm::bwd_workspace_layout(nullptr, batch, seqlen, d_inner, d_state, ssm::bwd_plan(batch, seqlen, d_inner), &total);
   return total;
 }
 
@@ -361,16 +361,19 @@ int bwd_impl(const void* x, const void* delta, const float* A, const void* B, co
       if (overlap(workspace, need, outs[k], outb[k])) return SSM_ERR_ALIAS;
   }
   const int64_t tiles = (d_inner + 63) / 64;
-  if (batch * tiles > INT32_MAX || (n_bc * 2 + 255) / 256 > INT32_MAX || (d_inner * d_state + 255) / 256 > INT32_MAX)
+  const ssm::BwdPlan bplan = ssm::bwd_plan(batch, seqlen, d_inner);
+  if (batch * tiles * bplan.n_chunks > INT32_MAX || (n_bc * 2 + 255) / 256 > INT32_MAX ||
+      (d_inner * d_state + 255) / 256 > INT32_MAX || (n_h + 255) / 256 > INT32_MAX)
     return SSM_ERR_BAD_DIM;
 
   if (d_inner == 0) return SSM_OK;
   float* ws = static_cast<float*>(workspace);
-  const ssm::BwdWorkspace lay = ssm::bwd_workspace_layout(ws, batch, seqlen, d_inner, d_state, nullptr);
+  const ssm::BwdPlan plan = ssm::bwd_plan(batch, seqlen, d_inner);
+  const ssm::BwdWorkspace lay = ssm::bwd_workspace_layout(ws, batch, seqlen, d_inner, d_state, plan, nullptr);
   ssm::BwdLaunch p{x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, ckpt, dx, ddelta, dA, dB, dC, dD, dz, dh0,
                    d_dt_bias, flags, batch, seqlen, d_inner, (int32_t)d_state, io_dtype == SSM_DTYPE_BF16,
                    static_cast<hipStream_t>(stream)};
-  return ssm::launch_scan_bwd(p, lay) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  return ssm::launch_scan_bwd(p, lay, plan) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 int conv_impl(const void* x, const float* w, const float* bias, const float* state_in, void* y, float* state_out,

@@ -39,6 +39,7 @@
 //   3. k_bwd_reduce_bc / k_bwd_reduce_params: sum the partials over tiles (dB,
 //      dC) and over batch rows (dA, dD, d_dt_bias) in a fixed order, so the
 //      result does not depend on scheduling.
+#include "scan_sweep.h"  // the forward summary sweep gives chunk entry states
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
@@ -53,7 +54,14 @@ constexpr int kRedStride = 68;  // LDS row stride in floats (64 lanes + 4 pad: r
 struct BwdDims {
   int64_t batch, seqlen, d_inner;
   int32_t tiles, nblk;
+  int32_t n_chunks, chunk_blocks;  // sequence chunks, blocks per chunk
 };
+
+// Blocks [kb, ke) of chunk c.
+__device__ __forceinline__ void chunk_blocks(const BwdDims& dm, int c, int& kb, int& ke) {
+  kb = c * dm.chunk_blocks;
+  ke = min(dm.nblk, kb + dm.chunk_blocks);
+}
 
 __device__ __forceinline__ float sigmoid(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
 
@@ -93,23 +101,30 @@ template <typename T, int N, int MODE>
 __global__ void __launch_bounds__(64)
     k_bwd_ckpt(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
                const T* __restrict__ B, const float* __restrict__ h0, const float* __restrict__ dt_bias,
-               float* __restrict__ ckpt, const BwdDims dm) {
+               float* __restrict__ ckpt, const float* __restrict__ h_entry, const BwdDims dm) {
   const int lane = threadIdx.x;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = bid % dm.tiles;
-  const int64_t b = bid / dm.tiles;
+  bid /= dm.tiles;
+  const int chunk = bid % dm.n_chunks;
+  const int64_t b = bid / dm.n_chunks;
   const int64_t DI = dm.d_inner, L = dm.seqlen;
   const int64_t d = (int64_t)tile * 64 + lane;
   const bool dvalid = d < DI;
   const int64_t dc = dvalid ? d : DI - 1;
   const int64_t cbase = (int64_t)tile * 64;
   const int lc = (int)(dc - cbase);
+  int kb, ke;
+  chunk_blocks(dm, chunk, kb, ke);
 
+  // Start state: h0 for one chunk, else the chunk's entry state.
+  const float* hs = h_entry != nullptr ? h_entry + (((int64_t)chunk * dm.batch + b) * DI + dc) * N
+                                       : (h0 != nullptr ? h0 + (b * DI + dc) * N : nullptr);
   float Al2[N], h[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     Al2[n] = A[dc * N + n] * kLog2e;
-    h[n] = h0 != nullptr ? h0[(b * DI + dc) * N + n] : 0.f;
+    h[n] = hs != nullptr ? hs[n] : 0.f;
   }
   const float dtb = (MODE & 1) ? dt_bias[dc] : 0.f;
   const uint32_t row_bytes = (uint32_t)(DI * (int64_t)sizeof(T));
@@ -122,8 +137,8 @@ __global__ void __launch_bounds__(64)
   const T* Bb = B + b * L * N;
   float* cp = ckpt + b * dm.nblk * N * DI + d;
 
-  // Only blocks 0 .. nblk-2 are stepped through (the state after the last
-  // block is not needed), and all of them are full.
+  // Only blocks kb .. ke-2 are stepped through (the state after the chunk's
+  // last block is not needed), and all of them are full.
   // Raw values: widening happens at use, so the next block's loads stay in
   // flight while this block computes.
   T xn[kBB], dn[kBB];
@@ -137,29 +152,29 @@ __global__ void __launch_bounds__(64)
     }
   };
   StateRow<T, N> bq;
-  if (dm.nblk > 1) {
-    fetch(0);
-    bq.load(Bb);
+  if (ke - kb > 1) {
+    fetch(kb);
+    bq.load(Bb + (int64_t)kb * kBB * N);
   }
-  for (int k = 0; k < dm.nblk; ++k) {
+  for (int k = kb; k < ke; ++k) {
     if (dvalid) {
 #pragma unroll
       for (int n = 0; n < N; ++n) cp[((int64_t)k * N + n) * DI] = h[n];
     }
-    if (k + 1 >= dm.nblk) break;
+    if (k + 1 >= ke) break;
     T xr[kBB], dr[kBB];
 #pragma unroll
     for (int i = 0; i < kBB; ++i) {
       xr[i] = xn[i];
       dr[i] = dn[i];
     }
-    if (k + 2 < dm.nblk) fetch(k + 1);
+    if (k + 2 < ke) fetch(k + 1);
 #pragma unroll
     for (int i = 0; i < kBB; ++i) {
       bq.touch();
       __builtin_amdgcn_sched_barrier(0);
       const StateRow<T, N> br = bq;
-      // The next row is at most (nblk - 1) * kBB < seqlen.
+      // The next row is at most (ke - 1) * kBB < seqlen.
       bq.load(Bb + ((int64_t)k * kBB + i + 1) * N);
       __builtin_amdgcn_sched_barrier(0);
       float dt = io_to_f32(dr[i]);
@@ -169,7 +184,105 @@ __global__ void __launch_bounds__(64)
       for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(hw_exp2(dt * Al2[n]), h[n], wx * br.get(n));
     }
   }
-  if (dm.nblk > 1) bq.touch();
+  if (ke - kb > 1) bq.touch();
+}
+
+// Adjoint summary of chunk c >= 1: processing its steps backwards maps the
+// incoming adjoint lam to P * lam + S (P = exp(A * sum delta) per state, S
+// the result from lam = 0), the same affine form as the forward carry.  P is
+// accumulated as the product of the very decays the sweep multiplies lam by:
+// for slowly decaying channels (small delta) this matches the unsplit sweep
+// far more closely than exp of the rounded sum.
+template <typename T, int N, int MODE>
+__global__ void __launch_bounds__(64)
+    k_bwd_lam_summary(const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ C,
+                      const T* __restrict__ z, const T* __restrict__ dy, const float* __restrict__ dt_bias,
+                      float* __restrict__ lP, float* __restrict__ lS, const BwdDims dm) {
+  const int lane = threadIdx.x;
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = bid % dm.tiles;
+  bid /= dm.tiles;
+  const int chunk = 1 + bid % (dm.n_chunks - 1);
+  const int64_t b = bid / (dm.n_chunks - 1);
+  const int64_t DI = dm.d_inner, L = dm.seqlen;
+  const int64_t d = (int64_t)tile * 64 + lane;
+  const bool dvalid = d < DI;
+  const int64_t dc = dvalid ? d : DI - 1;
+  const int64_t cbase = (int64_t)tile * 64;
+  const int lc = (int)(dc - cbase);
+  const bool has_z = z != nullptr;
+  int kb, ke;
+  chunk_blocks(dm, chunk, kb, ke);
+  const int64_t t_lo = (int64_t)kb * kBB, t_hi = min(L, (int64_t)ke * kBB);
+
+  float Al2[N], lam[N], P[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    Al2[n] = A[dc * N + n] * kLog2e;
+    lam[n] = 0.f;
+    P[n] = 1.f;
+  }
+  const float dtb = (MODE & 1) ? dt_bias[dc] : 0.f;
+  const uint32_t row_bytes = (uint32_t)(DI * (int64_t)sizeof(T));
+  const uint32_t lo = (uint32_t)lc * (uint32_t)sizeof(T);
+  auto rowp = [&](const void* base, int64_t t) {
+    return uniform_ptr(reinterpret_cast<const char*>(base) + ((b * L + t) * DI + cbase) * (int64_t)sizeof(T));
+  };
+  const T* Cb = C + b * L * N;
+  for (int64_t t1 = t_hi; t1 > t_lo; t1 -= kBB) {
+    const int64_t t0 = max(t_lo, t1 - kBB);
+    const int nt = (int)(t1 - t0);
+    const gchar* db = rowp(delta, t0);
+    const gchar* yb = rowp(dy, t0);
+    const gchar* zb = has_z ? rowp(z, t0) : db;
+    float dt[kBB], g[kBB];
+#pragma unroll
+    for (int i = 0; i < kBB; ++i) {
+      const uint32_t o = lo + (uint32_t)min(i, nt - 1) * row_bytes;
+      float v = gld<T>(db, o);
+      if (MODE & 1) v = softplus(v + dtb);
+      dt[i] = v;
+      const float dyv = dvalid ? gld<T>(yb, o) : 0.f;
+      const float zv = gld<T>(zb, o);
+      g[i] = has_z ? dyv * zv * sigmoid(zv) : dyv;
+    }
+#pragma unroll
+    for (int i = kBB - 1; i >= 0; --i) {
+      if (i < nt) {
+        StateRow<T, N> cr;
+        cr.load(Cb + (t0 + i) * N);
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+          const float a = hw_exp2(dt[i] * Al2[n]);
+          lam[n] = __builtin_fmaf(g[i], cr.get(n), lam[n]) * a;
+          P[n] *= a;
+        }
+      }
+    }
+  }
+  if (dvalid) {
+    const int64_t o = (((int64_t)(chunk - 1) * dm.batch + b) * DI + d) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      lP[o + n] = P[n];
+      lS[o + n] = lam[n];
+    }
+  }
+}
+
+// Incoming adjoint of every chunk, last first: lIn[c-1] = lP[c-1] * lIn[c] +
+// lS[c-1], lIn[n_chunks-1] = dh_last (or 0).  One lane per state.
+__global__ void __launch_bounds__(256) k_bwd_lam_carry(const float* __restrict__ dh_last,
+                                                       const float* __restrict__ lP, const float* __restrict__ lS,
+                                                       float* __restrict__ lIn, int64_t states, int64_t n_chunks) {
+  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (s >= states) return;
+  float v = dh_last != nullptr ? dh_last[s] : 0.f;
+  lIn[(n_chunks - 1) * states + s] = v;
+  for (int64_t c = n_chunks - 1; c >= 1; --c) {
+    v = __builtin_fmaf(lP[(c - 1) * states + s], v, lS[(c - 1) * states + s]);
+    lIn[(c - 1) * states + s] = v;
+  }
 }
 
 // Steps of abar * h_{t-1} a lane keeps in VGPRs at once.  With 16 states a
@@ -192,7 +305,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 const float* __restrict__ dt_bias, const float* __restrict__ ckpt, T* __restrict__ dx,
                 T* __restrict__ ddelta, T* __restrict__ dz, float* __restrict__ dh0, float* __restrict__ part_bc,
                 float* __restrict__ part_a, float* __restrict__ part_d, float* __restrict__ part_t,
-                const BwdDims dm) {
+                const float* __restrict__ lam_in, const BwdDims dm) {
   constexpr int SUB = bwd_sub<N>();                   // steps of w held at once
   constexpr int NSUB = kBB / SUB;                     // sub-blocks per block
   constexpr int GS = (64 / N) < SUB ? (64 / N) : SUB;  // steps per LDS reduction group
@@ -201,22 +314,29 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ __align__(16) float red[ROWS * kRedStride];
 
   const int lane = threadIdx.x;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = bid % dm.tiles;
-  const int64_t b = bid / dm.tiles;
+  bid /= dm.tiles;
+  const int chunk = bid % dm.n_chunks;
+  const int64_t b = bid / dm.n_chunks;
   const int64_t DI = dm.d_inner, L = dm.seqlen;
   const int64_t d = (int64_t)tile * 64 + lane;
   const bool dvalid = d < DI;
   const int64_t dc = dvalid ? d : DI - 1;
   const bool has_z = z != nullptr;
+  int kb, ke;
+  chunk_blocks(dm, chunk, kb, ke);
 
   // Lanes past d_inner run on a copy of the last channel with g = 0 and
-  // lam = 0, so every term they add to the channel sums is zero.
+  // lam = 0, so every term they add to the channel sums is zero.  The
+  // incoming adjoint is dh_last for one chunk, else the chunk's carry.
+  const float* li = lam_in != nullptr ? lam_in + (((int64_t)chunk * dm.batch + b) * DI + d) * N
+                                      : (dh_last != nullptr ? dh_last + (b * DI + d) * N : nullptr);
   float Al2[N], lam[N], gA[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     Al2[n] = A[dc * N + n] * kLog2e;
-    lam[n] = (dvalid && dh_last != nullptr) ? dh_last[(b * DI + d) * N + n] : 0.f;
+    lam[n] = (dvalid && li != nullptr) ? li[n] : 0.f;
     gA[n] = 0.f;
   }
   const float Dv = D != nullptr ? D[dc] : 0.f;
@@ -407,7 +527,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
           if (i < hi) {
             StateRow<T, N> br, cr;
             take(br, cr);
-            issue(i > lo ? t0 + i - 1 : (j > 0 ? t0 : (k > 0 ? t0 - kBB : t0)));
+            issue(i > lo ? t0 + i - 1 : (j > 0 ? t0 : (k > kb ? t0 - kBB : t0)));
             // The decays are recomputed here rather than kept from the
             // forward pass (that would hold another SUB * N values in
             // VGPRs); the empty asm keeps the compiler from merging the two
@@ -450,23 +570,24 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     }
   };
 
-  if (dm.nblk > 0) {
-    issue((int64_t)(dm.nblk - 1) * kBB);
-    for (int k = dm.nblk - 1; k >= 0; --k) block(k);
+  if (ke > kb) {
+    issue((int64_t)(ke - 1) * kBB);
+    for (int k = ke - 1; k >= kb; --k) block(k);
     // Let the last row request land before the wave ends.
     bq.touch();
     cq.touch();
   }
 
   if (dvalid) {
-    if (dh0 != nullptr) {
+    if (dh0 != nullptr && chunk == 0) {
 #pragma unroll
       for (int n = 0; n < N; ++n) dh0[(b * DI + d) * N + n] = lam[n];
     }
+    const int64_t row = (int64_t)chunk * dm.batch + b;
 #pragma unroll
-    for (int n = 0; n < N; ++n) part_a[(b * DI + d) * N + n] = gA[n];
-    part_d[b * DI + d] = accD;
-    part_t[b * DI + d] = accT;
+    for (int n = 0; n < N; ++n) part_a[(row * DI + d) * N + n] = gA[n];
+    part_d[row * DI + d] = accD;
+    part_t[row * DI + d] = accT;
   }
 }
 
@@ -517,27 +638,54 @@ __global__ void __launch_bounds__(256) k_bwd_reduce_params(const float* __restri
 }
 
 template <typename T, int N, int MODE>
-hipError_t launch_bwd_t(const BwdLaunch& p, const BwdWorkspace& ws) {
+hipError_t launch_bwd_t(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPlan& pl) {
   const int64_t tiles = (p.d_inner + 63) / 64;
-  const BwdDims dm{p.batch, p.seqlen, p.d_inner, (int32_t)tiles, (int32_t)((p.seqlen + kBB - 1) / kBB)};
+  const int nch = (int)pl.n_chunks;
+  const BwdDims dm{p.batch, p.seqlen, p.d_inner, (int32_t)tiles, (int32_t)((p.seqlen + kBB - 1) / kBB), nch,
+                   (int32_t)(pl.chunk_len / kBB)};
   const T* x = static_cast<const T*>(p.x);
   const T* dl = static_cast<const T*>(p.delta);
   const T* Bm = static_cast<const T*>(p.B);
   const T* Cm = static_cast<const T*>(p.C);
+  const T* zz = static_cast<const T*>(p.z);
+  const T* dyy = static_cast<const T*>(p.dy);
+  const int64_t states = p.batch * p.d_inner * N;
   hipError_t e;
   const unsigned waves = (unsigned)(p.batch * tiles);
   if (waves > 0) {
     const float* ck = p.ckpt;
     if (ck == nullptr && dm.nblk > 0) {
-      e = launch(k_bwd_ckpt<T, N, MODE>, dim3(waves), dim3(64), 0, p.stream, x, dl, p.A, Bm, p.h0, p.dt_bias,
-                 ws.ckpt, dm);
+      const float* h_entry = nullptr;
+      if (nch > 1) {
+        // Entry state of every chunk: the forward scan's chunk summaries
+        // (k_scan_sweep in summary mode) and their carry.
+        SweepDims sd{p.batch, p.seqlen, p.d_inner, pl.chunk_len, (int32_t)tiles, nch - 1, nch, 0, nullptr};
+        e = launch(k_scan_sweep<T, N, N, true, MODE>, dim3((unsigned)(p.batch * (nch - 1) * tiles)), dim3(64), 0,
+                   p.stream, x, dl, p.A, Bm, Cm, (const float*)nullptr, zz, (const float*)nullptr, (T*)nullptr,
+                   (float*)nullptr, ws.fP, ws.fS, p.dt_bias, sd);
+        if (e != hipSuccess) return e;
+        e = launch_chunk_carry(p.h0, ws.fP, ws.fS, ws.fH, states, nch, p.stream);
+        if (e != hipSuccess) return e;
+        h_entry = ws.fH;
+      }
+      e = launch(k_bwd_ckpt<T, N, MODE>, dim3(waves * nch), dim3(64), 0, p.stream, x, dl, p.A, Bm, p.h0,
+                 p.dt_bias, ws.ckpt, h_entry, dm);
       if (e != hipSuccess) return e;
       ck = ws.ckpt;
     }
-    e = launch(k_bwd_sweep<T, N, MODE>, dim3(waves), dim3(64), 0, p.stream, x, dl, p.A, Bm, Cm, p.D,
-               static_cast<const T*>(p.z), static_cast<const T*>(p.dy), p.dh_last, p.dt_bias, ck,
-               static_cast<T*>(p.dx), static_cast<T*>(p.ddelta), static_cast<T*>(p.dz), p.dh0, ws.part_bc,
-               ws.part_a, ws.part_d, ws.part_t, dm);
+    const float* lam_in = nullptr;
+    if (nch > 1) {
+      e = launch(k_bwd_lam_summary<T, N, MODE>, dim3((unsigned)(p.batch * (nch - 1) * tiles)), dim3(64), 0,
+                 p.stream, dl, p.A, Cm, zz, dyy, p.dt_bias, ws.lP, ws.lS, dm);
+      if (e != hipSuccess) return e;
+      e = launch(k_bwd_lam_carry, dim3((unsigned)((states + 255) / 256)), dim3(256), 0, p.stream, p.dh_last, ws.lP,
+                 ws.lS, ws.lIn, states, (int64_t)nch);
+      if (e != hipSuccess) return e;
+      lam_in = ws.lIn;
+    }
+    e = launch(k_bwd_sweep<T, N, MODE>, dim3(waves * nch), dim3(64), 0, p.stream, x, dl, p.A, Bm, Cm, p.D, zz, dyy,
+               p.dh_last, p.dt_bias, ck, static_cast<T*>(p.dx), static_cast<T*>(p.ddelta), static_cast<T*>(p.dz),
+               p.dh0, ws.part_bc, ws.part_a, ws.part_d, ws.part_t, lam_in, dm);
     if (e != hipSuccess) return e;
   }
   const int64_t rows = p.batch * p.seqlen;
@@ -549,35 +697,61 @@ hipError_t launch_bwd_t(const BwdLaunch& p, const BwdWorkspace& ws) {
   }
   const int64_t na = p.d_inner * N;
   if (na > 0) {
+    // Partials are [chunk][batch] rows: sum over both.
     e = launch(k_bwd_reduce_params, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, p.stream, ws.part_a,
-               ws.part_d, ws.part_t, p.dA, p.dD, p.d_dt_bias, p.batch, p.d_inner, (int32_t)N);
+               ws.part_d, ws.part_t, p.dA, p.dD, p.d_dt_bias, p.batch * nch, p.d_inner, (int32_t)N);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 template <typename T, int MODE>
-hipError_t launch_bwd_n(const BwdLaunch& p, const BwdWorkspace& ws) {
+hipError_t launch_bwd_n(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPlan& pl) {
   switch (p.d_state) {
-    case 2: return launch_bwd_t<T, 2, MODE>(p, ws);
-    case 4: return launch_bwd_t<T, 4, MODE>(p, ws);
-    case 8: return launch_bwd_t<T, 8, MODE>(p, ws);
-    case 16: return launch_bwd_t<T, 16, MODE>(p, ws);
+    case 2: return launch_bwd_t<T, 2, MODE>(p, ws, pl);
+    case 4: return launch_bwd_t<T, 4, MODE>(p, ws, pl);
+    case 8: return launch_bwd_t<T, 8, MODE>(p, ws, pl);
+    case 16: return launch_bwd_t<T, 16, MODE>(p, ws, pl);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
+// Waves the backward sweep aims for (256 CUs x 4 SIMDs x 2) and the
+// shortest chunk it cuts a sequence into.
+constexpr int64_t kBwdTargetWaves = 2048;
+constexpr int64_t kBwdMinChunk = 256;
+
+BwdPlan bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner) {
+  const int64_t waves = batch * ((d_inner + 63) / 64);
+  int64_t nch = 1;
+  if (waves > 0 && waves < kBwdTargetWaves && seqlen >= 2 * kBwdMinChunk) {
+    nch = (kBwdTargetWaves + waves - 1) / waves;
+    if (nch > seqlen / kBwdMinChunk) nch = seqlen / kBwdMinChunk;
+  }
+  const int64_t nblk = (seqlen + kBB - 1) / kBB;
+  int64_t cb = nblk > 0 ? (nblk + nch - 1) / nch : 1;  // blocks per chunk
+  if (cb < 1) cb = 1;
+  BwdPlan p;
+  p.chunk_len = cb * kBB;
+  p.n_chunks = nblk > 0 ? (nblk + cb - 1) / cb : 1;
+  return p;
+}
+
 BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                                  int64_t* total_floats) {
+                                  const BwdPlan& plan, int64_t* total_floats) {
   auto up = [](int64_t v) { return (v + 63) / 64 * 64; };  // 256-byte sections
   const int64_t tiles = (d_inner + 63) / 64;
   const int64_t nblk = (seqlen + kBB - 1) / kBB;
+  const int64_t nch = plan.n_chunks;
+  const int64_t states = batch * d_inner * d_state;
   const int64_t n_ck = up(batch * nblk * d_state * d_inner);
   const int64_t n_bc = up(tiles * batch * seqlen * 2 * d_state);
-  const int64_t n_a = up(batch * d_inner * d_state);
-  const int64_t n_d = up(batch * d_inner);
+  const int64_t n_a = up(nch * states);
+  const int64_t n_d = up(nch * batch * d_inner);
+  const int64_t n_sum = nch > 1 ? up((nch - 1) * states) : 0;
+  const int64_t n_ent = nch > 1 ? up(nch * states) : 0;
   BwdWorkspace ws{};
   if (base != nullptr) {
     ws.ckpt = base;
@@ -585,14 +759,20 @@ BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, in
     ws.part_a = ws.part_bc + n_bc;
     ws.part_d = ws.part_a + n_a;
     ws.part_t = ws.part_d + n_d;
+    ws.fP = ws.part_t + n_d;
+    ws.fS = ws.fP + n_sum;
+    ws.fH = ws.fS + n_sum;
+    ws.lP = ws.fH + n_ent;
+    ws.lS = ws.lP + n_sum;
+    ws.lIn = ws.lS + n_sum;
   }
-  if (total_floats != nullptr) *total_floats = n_ck + n_bc + n_a + 2 * n_d;
+  if (total_floats != nullptr) *total_floats = n_ck + n_bc + n_a + 2 * n_d + 4 * n_sum + 2 * n_ent;
   return ws;
 }
 
-hipError_t launch_scan_bwd(const BwdLaunch& p, const BwdWorkspace& ws) {
-  if (p.flags & 1u) return p.bf16 ? launch_bwd_n<uint16_t, 1>(p, ws) : launch_bwd_n<float, 1>(p, ws);
-  return p.bf16 ? launch_bwd_n<uint16_t, 0>(p, ws) : launch_bwd_n<float, 0>(p, ws);
+hipError_t launch_scan_bwd(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPlan& pl) {
+  if (p.flags & 1u) return p.bf16 ? launch_bwd_n<uint16_t, 1>(p, ws, pl) : launch_bwd_n<float, 1>(p, ws, pl);
+  return p.bf16 ? launch_bwd_n<uint16_t, 0>(p, ws, pl) : launch_bwd_n<float, 0>(p, ws, pl);
 }
 
 }  // namespace ssm

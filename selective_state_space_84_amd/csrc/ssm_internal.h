@@ -116,21 +116,41 @@ struct BwdLaunch {
 // Steps per checkpoint block of the backward pass.
 constexpr int kBwdBlock = 8;
 
-// Sections of the backward workspace (floats, each 256-byte aligned):
+// Sequence chunks of the backward pass: (chunk_len, n_chunks), chunk_len a
+// multiple of kBwdBlock.  Chunks are used only when channels alone leave the
+// chip idle; they add a forward summary (standalone calls) and a reverse
+// adjoint summary.
+struct BwdPlan {
+  int64_t chunk_len;
+  int64_t n_chunks;
+};
+BwdPlan bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner);
+
+// Sections of the backward workspace (floats, each 256-byte aligned), with
+// S = batch * d_inner * d_state states and c = n_chunks:
 //   ckpt    [batch][ceil(seqlen/8)][d_state][d_inner]  states at block starts
 //   part_bc [tiles][batch][seqlen][2*d_state]          per-tile dB | dC sums
-//   part_a  [batch][d_inner][d_state]                  per-row dA
-//   part_d, part_t [batch][d_inner]                    per-row dD, d_dt_bias
+//   part_a  [c][batch][d_inner][d_state]               per-(chunk, row) dA
+//   part_d, part_t [c][batch][d_inner]                 per-(chunk, row) dD, d_dt_bias
+//   when c > 1: forward chunk summaries fP, fS [c-1][S] and entry states fH
+//   [c][S]; adjoint chunk summaries lP, lS [c-1][S] and incoming adjoints
+//   lIn [c][S].
 struct BwdWorkspace {
   float* ckpt;
   float* part_bc;
   float* part_a;
   float* part_d;
   float* part_t;
+  float* fP;
+  float* fS;
+  float* fH;
+  float* lP;
+  float* lS;
+  float* lIn;
 };
 BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                                  int64_t* total_floats);
-hipError_t launch_scan_bwd(const BwdLaunch& p, const BwdWorkspace& ws);
+                                  const BwdPlan& plan, int64_t* total_floats);
+hipError_t launch_scan_bwd(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPlan& pl);
 
 hipError_t launch_scan(const ScanLaunch& p);
 template <int MODE>

@@ -8,10 +8,12 @@ and batch rows) is compared with the fp64 oracle under the floored metric.
 The error of ddelta grows with the memory of the slowest channels: ddelta_t =
 sum_n lam_t (A abar_t h_{t-1} + B_t x_t), and where delta is small abar stays
 close to 1, so lam and h grow like the square root of the number of steps they
-remember and the two terms cancel more and more.  On a 1000-step case this
-emulation already reaches several 1e-5, so BWD_F32_GATE = 2e-4 leaves room for
-the hardware's 1-ulp exp2 and the device's summation orders; all other
-gradients stay near 1e-5.
+remember and the two terms cancel more and more.  On ~1000-step cases the
+emulation with correctly rounded exp2 reaches 4e-5 to 7e-5; with each exp2
+result off by a random -1, 0 or +1 ulp (the accuracy of the hardware's
+v_exp_f32) it reaches up to ~1.2e-4.  BWD_F32_GATE = 5e-4 leaves 4x room over
+that model; every other gradient stays near 1e-5.  A real mistake (a dropped
+term, a decay from the wrong step) costs percent-level errors.
 
 The emulation is test-side arithmetic only (neither the oracle nor the device
 path); it restates the fp32 steps of the kernel for one purpose: to size the
@@ -23,7 +25,7 @@ import oracle
 from conftest import floored_rel_err
 from selective_state_space_84_amd import inputs
 
-BWD_F32_GATE = 2e-4
+BWD_F32_GATE = 5e-4
 
 f = np.float32
 L2E = f(1.4426950408889634)
@@ -34,11 +36,21 @@ def _exp2(v):
     return np.exp2(v.astype(np.float64)).astype(np.float32)
 
 
-def _sigmoid(v):
-    return (f(1) / (f(1) + _exp2((-v * L2E).astype(np.float32)))).astype(np.float32)
+_ULP_RNG = None
 
 
-def _emulate_bwd(inp, gr):
+def _exp2_1ulp(v):
+    """exp2 off by a random -1, 0 or +1 ulp (a model of v_exp_f32's accuracy)."""
+    r = _exp2(v)
+    k = _ULP_RNG.integers(-1, 2, size=r.shape).astype(np.int32)
+    return np.where(r > 0, (r.view(np.int32) + k).view(np.float32), r).astype(np.float32)
+
+
+def _sigmoid(v, exp2=_exp2):
+    return (f(1) / (f(1) + exp2((-v * L2E).astype(np.float32)))).astype(np.float32)
+
+
+def _emulate_bwd(inp, gr, exp2=_exp2):
     x, dl, A, Bm, Cm, Dv, z, h0 = (inp[k] for k in ("x", "delta", "A", "B", "C", "D", "z", "h0"))
     dy, dhl = gr["dy"], gr["dh_last"]
     batch, L, d_inner = x.shape
@@ -48,7 +60,7 @@ def _emulate_bwd(inp, gr):
     ws = np.empty((L, batch, d_inner, N), np.float32)  # abar * h_{t-1}
     hs = np.empty((L, batch, d_inner, N), np.float32)
     for t in range(L):
-        a = _exp2((dl[:, t, :, None] * Al2[None]).astype(np.float32))
+        a = exp2((dl[:, t, :, None] * Al2[None]).astype(np.float32))
         w = (a * h).astype(np.float32)
         dtx = (dl[:, t] * x[:, t]).astype(np.float32)
         h = (w + dtx[:, :, None] * Bm[:, t, None, :]).astype(np.float32)
@@ -62,7 +74,7 @@ def _emulate_bwd(inp, gr):
     dC = np.empty(Cm.shape, np.float32)
     dD = np.zeros((batch, d_inner), np.float32)
     for t in range(L - 1, -1, -1):
-        s = _sigmoid(z[:, t])
+        s = _sigmoid(z[:, t], exp2)
         g = (dy[:, t] * z[:, t] * s).astype(np.float32)
         ypre = (Dv[None] * x[:, t]).astype(np.float32)
         for n in range(N):
@@ -79,7 +91,7 @@ def _emulate_bwd(inp, gr):
             dA[:, :, n] = (dA[:, :, n] + dl[:, t] * tw).astype(np.float32)
             sb = (sb + lam[:, :, n] * Bm[:, t, None, n]).astype(np.float32)
         dB[:, t] = np.einsum("bdn,bd->bn", lam.astype(np.float64), dtx.astype(np.float64)).astype(np.float32)
-        lam = (lam * _exp2((dl[:, t, :, None] * Al2[None]).astype(np.float32))).astype(np.float32)
+        lam = (lam * exp2((dl[:, t, :, None] * Al2[None]).astype(np.float32))).astype(np.float32)
         dx[:, t] = (g * Dv[None] + dl[:, t] * sb).astype(np.float32)
         dd_out[:, t] = (dd * LN2 + x[:, t] * sb).astype(np.float32)
         dD = (dD + g * x[:, t]).astype(np.float32)
@@ -101,3 +113,21 @@ def test_backward_fp32_floor_sizes_the_gate():
     # ... and ddelta is the gradient that needs the looser gate: plain fp32
     # arithmetic in this order already exceeds the forward's 1e-5.
     assert errs["ddelta"] > 1e-5
+
+
+def test_backward_fp32_floor_with_hardware_exp2_model():
+    """The 1013-step case of the GPU chunk tests, with exp2 off by up to one ulp."""
+    global _ULP_RNG
+    seed = 1700 + 1013 + 16
+    inp = inputs.make_scan_inputs(2, 1013, 70, 16, "f32", seed, nonzero_h0=True)
+    gr = inputs.make_scan_grads(2, 1013, 70, 16, "f32", seed)
+    ref = oracle.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
+                          dy=gr["dy"], dh_last=gr["dh_last"])
+    worst = 0.0
+    for trial in range(3):
+        _ULP_RNG = np.random.default_rng(trial)
+        emu = _emulate_bwd(inp, gr, exp2=_exp2_1ulp)
+        errs = {k: floored_rel_err(emu[k], ref[k]) for k in emu}
+        print("trial", trial, " ".join("%s %.2e" % kv for kv in errs.items()))
+        worst = max(worst, max(errs.values()))
+    assert worst <= BWD_F32_GATE / 3
