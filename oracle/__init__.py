@@ -17,7 +17,9 @@ filter, a library ZOH discretisation and brute-force unrolled sums by the
 CPU tests (``tests/test_oracle_pins.py``, ``tests/test_oracle_conv_pins.py``);
 the gradient ``scan_bwd`` against central finite differences of ``scan``,
 Euler identities of the parts of the scan that are linear, and hand-derived
-one-step derivatives (``tests/test_oracle_bwd_pins.py``).
+one-step derivatives (``tests/test_oracle_bwd_pins.py``); ``ssd`` against the
+Mamba-1 scan with the decay broadcast over states, the section 6.1 masked
+matrix, and a block (chunked) decomposition (``tests/test_oracle_ssd_pins.py``).
 """
 from __future__ import annotations
 
@@ -64,6 +66,8 @@ def _load():
     lib.ssm_oracle_conv1d_f64.restype = ctypes.c_int
     lib.ssm_oracle_scan_bwd_f64.argtypes = [P] * 20 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
     lib.ssm_oracle_scan_bwd_f64.restype = ctypes.c_int
+    lib.ssm_oracle_ssd_f64.argtypes = [P] * 11 + [I64] * 6 + [ctypes.c_int]
+    lib.ssm_oracle_ssd_f64.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -168,6 +172,32 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dt_bias=None, *, dy, dh
     if rc != 0:
         raise ValueError("oracle scan_bwd rejected its arguments (%d)" % rc)
     return g
+
+
+def ssd(x, dt, A, B, C, D=None, z=None, h0=None, dt_bias=None, *, delta_softplus=False):
+    """Scan with a scalar decay per head (Mamba-2 / SSD form).
+
+    Shapes: x, z: (batch, seqlen, nheads, headdim); dt: (batch, seqlen, nheads);
+    A, D, dt_bias: (nheads,); B, C: (batch, seqlen, ngroups, d_state);
+    h0: (batch, nheads, headdim, d_state).  Returns (y, h_last) in fp64.
+    """
+    lib = _load()
+    x, dt, A, B, C = (to_f64(v) for v in (x, dt, A, B, C))
+    D, z, h0, dt_bias = (to_f64(v) for v in (D, z, h0, dt_bias))
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, d_state = B.shape[2], B.shape[3]
+    assert dt.shape == (batch, seqlen, nheads) and A.shape == (nheads,)
+    assert B.shape == (batch, seqlen, ngroups, d_state) and C.shape == B.shape
+    assert z is None or z.shape == x.shape
+    assert h0 is None or h0.shape == (batch, nheads, headdim, d_state)
+    y = np.empty_like(x)
+    h_last = np.empty((batch, nheads, headdim, d_state))
+    rc = lib.ssm_oracle_ssd_f64(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                _ptr(dt_bias), _ptr(y), _ptr(h_last), batch, seqlen, nheads, headdim, ngroups,
+                                d_state, 1 if delta_softplus else 0)
+    if rc != 0:
+        raise ValueError("oracle ssd rejected its arguments (%d)" % rc)
+    return y, h_last
 
 
 def scan_channels(inputs, channels, *, exact_zoh=False, delta_softplus=False):

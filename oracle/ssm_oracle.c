@@ -373,4 +373,70 @@ int ssm_oracle_scan_bwd_f64(const double* x, const double* delta, const double* 
   return ORACLE_OK;
 }
 
-int ssm_oracle_version(void) { return 3; }
+/*
+ * Mamba-2 style scan with a scalar decay per head (the SSD form).
+ * "Deriving and implementing Mamba from scratch" (dpshk.com/news/3333417),
+ * section 6.1: when A is a scalar per step the scan is y = M x with the
+ * lower-triangular M[k,i] = c_k (prod_{j=i+1..k} a_j) b_i, whose rank is
+ * bounded by the state size; section 6.2: A is a scalar, and groups of heads
+ * share B and C (like grouped-query attention).  "SSMs for long-document QA"
+ * (pwwt.cn/news/5168881), section 2.3: multi-head SSM, the state split over
+ * heads.  Per batch row b, head h (group g = h / (nheads / ngroups)),
+ * channel p of the head and state n:
+ *     a        = exp(dt[b,t,h] * A[h])
+ *     H[p,n]   = a * H[p,n] + dt[b,t,h] * B[b,t,g,n] * x[b,t,h,p]
+ *     y[b,t,h,p] = (sum_n C[b,t,g,n] * H[p,n] + D[h] * x[b,t,h,p]) * silu(z[b,t,h,p])
+ * (the input term dt*B follows the Mamba convention Bbar = delta*B).
+ *   x, z, y : [batch][seqlen][nheads][headdim]
+ *   dt      : [batch][seqlen][nheads] (delta_mode 1: softplus(dt + dt_bias[h]))
+ *   A, D, dt_bias : [nheads]   (D, z nullable)
+ *   B, C    : [batch][seqlen][ngroups][d_state]
+ *   h0, h_last : [batch][nheads][headdim][d_state] (nullable)
+ */
+int ssm_oracle_ssd_f64(const double* x, const double* dt, const double* A, const double* B, const double* C,
+                       const double* D, const double* z, const double* h0, const double* dt_bias, double* y,
+                       double* h_last, int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t ngroups, int64_t d_state, int delta_mode) {
+  if (!x || !dt || !A || !B || !C || !y) return ORACLE_BAD_ARG;
+  if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0 || ngroups <= 0 || d_state <= 0) return ORACLE_BAD_ARG;
+  if (nheads % ngroups != 0) return ORACLE_BAD_ARG;
+  if (delta_mode != 0 && delta_mode != 1) return ORACLE_BAD_ARG;
+  if (delta_mode == 1 && !dt_bias) return ORACLE_BAD_ARG;
+  const int64_t N = d_state, P = headdim, HP = nheads * headdim;
+  double* state = (double*)malloc((size_t)N * sizeof(double));
+  if (!state) return ORACLE_BAD_ARG;
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t h = 0; h < nheads; ++h) {
+      const int64_t g = h / (nheads / ngroups);
+      for (int64_t p = 0; p < P; ++p) {
+        for (int64_t n = 0; n < N; ++n) state[n] = h0 ? h0[((b * nheads + h) * P + p) * N + n] : 0.0;
+        for (int64_t t = 0; t < seqlen; ++t) {
+          double d = dt[(b * seqlen + t) * nheads + h];
+          if (delta_mode == 1) d = oracle_softplus(d + dt_bias[h]);
+          const double a = exp(d * A[h]);
+          const int64_t io = (b * seqlen + t) * HP + h * P + p;
+          const double xv = x[io];
+          const double* Bt = B + ((b * seqlen + t) * ngroups + g) * N;
+          const double* Ct = C + ((b * seqlen + t) * ngroups + g) * N;
+          double acc = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            state[n] = a * state[n] + d * Bt[n] * xv;
+            acc += Ct[n] * state[n];
+          }
+          double yv = acc + (D ? D[h] : 0.0) * xv;
+          if (z) {
+            const double zv = z[io];
+            yv = yv * (zv / (1.0 + exp(-zv)));
+          }
+          y[io] = yv;
+        }
+        if (h_last)
+          for (int64_t n = 0; n < N; ++n) h_last[((b * nheads + h) * P + p) * N + n] = state[n];
+      }
+    }
+  }
+  free(state);
+  return ORACLE_OK;
+}
+
+int ssm_oracle_version(void) { return 4; }
