@@ -13,7 +13,7 @@ states, 1000 consecutive in-place steps), and the fp64 CPU oracle on a
 bounded sample of the scan workload.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-decode] [--no-conv] [--no-bwd] [--no-cpu-baseline]
+                       [--no-decode] [--no-conv] [--no-bwd] [--no-ssd] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -50,7 +50,7 @@ def bwd_slots_per_element(d_state: int) -> int:
 def _kernel_source_sha() -> str:
     h = hashlib.sha256()
     for f in ("scan_sweep.h", "scan_mode0.hip", "scan_aux.hip", "update_kernel.hip", "conv_kernels.hip",
-              "scan_bwd.hip", "ssm_device.h", "ssm_internal.h"):
+              "scan_bwd.hip", "ssd_kernel.hip", "ssm_device.h", "ssm_internal.h"):
         with open(os.path.join(REPO, "selective_state_space_84_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -254,6 +254,52 @@ def bench_bwd(cfg, inp, steps, dev):
             "workspace_bytes": int(ws.numel()), "ckpt_bytes": int(ck.numel() * 4)}
 
 
+def bench_ssd(steps, dev):
+    """Scan with a scalar decay per head (Mamba-2 / SSD form) on the
+    Mamba-2 2.7B layer shape, evaluated chunk-wise on the matrix cores."""
+    import torch
+    from selective_state_space_84_amd import binding, inputs
+    cfg = inputs.SSD_2P7B
+    t0 = time.time()
+    inp = inputs.make_ssd_inputs(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.d_state, cfg.seed)
+    gen_s = time.time() - t0
+    d = {k: to_dev(inp.get(k), dev) for k in ("x", "dt", "A", "B", "C", "D", "z")}
+    y = torch.empty_like(d["x"])
+    hl = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state), dtype=torch.float32, device=dev)
+
+    def step():
+        binding.ssm_ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], y=y, h_last=hl)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    el = cfg.batch * cfg.seqlen * cfg.nheads * cfg.headdim
+    alg = (3 * el * 2 + cfg.batch * cfg.seqlen * cfg.nheads * 2 + 2 * cfg.batch * cfg.seqlen * cfg.ngroups * cfg.d_state * 2
+           + 2 * cfg.nheads * 4 + cfg.batch * cfg.nheads * cfg.headdim * cfg.d_state * 4)
+    # Matrix-core work as issued per 64-step chunk and (row, head): scores 10
+    # causal 16x16 tiles x N/32 steps; masked scores x X and C x H_prev and
+    # the state update with hi/lo operand pairs; 16x16x32 products.
+    nk = cfg.d_state // 32
+    mfma = 10 * nk + 48 + 4 * 4 * nk * 2 + 4 * (cfg.d_state // 16) * 2 * 2
+    flops = mfma * 16 * 16 * 32 * 2 * (-(-cfg.seqlen // 64)) * cfg.batch * cfg.nheads
+    gbps = alg / (ms * 1e-3) / 1e9
+    return {"workload": "%s ssd (batch %d, L %d, %d heads x %d, d_state %d, bf16 io)" % (
+                cfg.name, cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.d_state),
+            "steps": steps, "ms_per_step": round(ms, 6), "elements_per_s": round(el / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": alg},
+            "mfma": {"tflops_issued": round(flops / (ms * 1e-3) / 1e12, 2), "peak_bf16_tflops": 2500.0},
+            "input_gen_s": round(gen_s, 1)}
+
+
 def cpu_baseline(cfg, inp, y_dev, hl_dev, budget_s=12.0, flags=0):
     """fp64 oracle (single thread) on whole batch rows of the same workload,
     row after row until the time budget is spent; also compares those rows'
@@ -308,6 +354,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--n-split", type=int, default=0, help="override the launch plan (tuning)")
     ap.add_argument("--chunk-len", type=int, default=0, help="override the launch plan (tuning)")
@@ -380,6 +427,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_decode:
         out["decode"] = bench_decode(args.decode_steps, dev)
+        torch.cuda.empty_cache()
+    if not args.no_ssd:
+        out["ssd"] = bench_ssd(args.steps, dev)
     print(json.dumps(out), flush=True)
 
 

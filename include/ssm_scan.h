@@ -6,6 +6,7 @@
  *   ssm_scan_fwd      full-sequence selective scan (training / prefill)
  *   ssm_state_update  one recurrent step on a resident state (decode)
  *   ssm_scan_bwd      gradient of the full-sequence scan (training)
+ *   ssm_ssd_fwd       scan with a scalar decay per head (Mamba-2 / SSD form)
  *   ssm_conv1d_fwd / ssm_conv1d_update
  *                     the causal depthwise convolution that feeds the scan,
  *                     and its decode step
@@ -265,6 +266,40 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
                  const float* ckpt, void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* dh0,
                  float* d_dt_bias, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                  int32_t io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Scan with a scalar decay per head (the Mamba-2 / SSD form).  Per batch row
+ * b, head h (group g = h / (nheads / ngroups) of heads sharing B and C),
+ * channel p of the head and state n:
+ *
+ *   a         = exp(dt[b,t,h] * A[h])
+ *   H[p,n]    = a * H[p,n] + dt[b,t,h] * B[b,t,g,n] * x[b,t,h,p]
+ *   y[b,t,h,p] = (sum_n C[b,t,g,n] * H[p,n] + D[h] * x[b,t,h,p]) * silu(z[b,t,h,p])
+ *
+ * "Deriving and implementing Mamba from scratch" (dpshk.com/news/3333417),
+ * section 6.1 (a scalar decay makes the scan a lower-triangular
+ * semiseparable matrix, y = M x) and 6.2 (scalar A, groups of heads sharing
+ * B and C); "SSMs for long-document QA" (pwwt.cn/news/5168881), section 2.3
+ * (multi-head SSM, block-wise decomposition).  The kernel evaluates it chunk
+ * by chunk with matrix products on the matrix cores (bf16 operands, fp32
+ * accumulation, fp32 state).
+ *
+ *   x, z, y   : [batch][seqlen][nheads][headdim] bf16; x, z, y 16-byte aligned
+ *   dt        : [batch][seqlen][nheads] bf16 (the step, or the raw value with
+ *               SSM_FLAG_DELTA_SOFTPLUS: softplus(dt + dt_bias[h]))
+ *   A, D, dt_bias : [nheads] fp32 (D may be NULL; dt_bias only with the flag)
+ *   B, C      : [batch][seqlen][ngroups][d_state] bf16, 16-byte aligned
+ *   z         : NULL for no gate
+ *   h0, h_last: [batch][nheads][headdim][d_state] fp32, or NULL (zeros / not
+ *               written); h_last may be the h0 buffer
+ *   io_dtype  : SSM_DTYPE_BF16 only; headdim: 64; d_state: 64 or 128;
+ *   nheads a multiple of ngroups.  Other values: SSM_ERR_UNSUPPORTED.
+ * No workspace.  Same conventions, validation and error codes as the scan.
+ */
+int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                const void* z, const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen,
+                int64_t nheads, int64_t headdim, int64_t ngroups, int64_t d_state, int32_t io_dtype, uint32_t flags,
+                const float* dt_bias, void* stream);
 
 /*
  * Causal depthwise conv1d over time, optionally followed by SiLU: the step

@@ -58,6 +58,7 @@ SIGNATURES = {
     "ssm_scan_bwd_workspace_size": ([_I64, _I64, _I64, _I64], _SZ),
     "ssm_scan_ckpt_bytes": ([_I64, _I64, _I64, _I64], _SZ),
     "ssm_scan_bwd": ([_P] * 21 + [_I64] * 4 + [_I32, _U32, _P, _SZ, _P], ctypes.c_int),
+    "ssm_ssd_fwd": ([_P] * 10 + [_I64] * 6 + [_I32, _U32, _P, _P], ctypes.c_int),
     "ssm_conv1d_fwd": ([_P] * 6 + [_I64] * 4 + [_I32, _I32, _P], ctypes.c_int),
     "ssm_conv1d_update": ([_P] * 5 + [_I64] * 3 + [_I32, _I32, _P], ctypes.c_int),
 }
@@ -261,6 +262,29 @@ def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None
     if rc != SSM_OK:
         raise SsmError(rc, "ssm_scan_bwd")
     return g
+
+
+def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, h0=None, *, y=None, h_last=None, want_h_last=True, flags=0,
+                dt_bias=None, stream=None):
+    """Scan with a scalar decay per head (Mamba-2 / SSD form); returns (y, h_last).
+
+    x, z: (batch, seqlen, nheads, 64) bf16; dt: (batch, seqlen, nheads) bf16;
+    A, D, dt_bias: (nheads,) fp32; B, C: (batch, seqlen, ngroups, d_state) bf16;
+    h0: (batch, nheads, 64, d_state) fp32.
+    """
+    import torch
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, d_state = B.shape[2], B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    if h_last is None and want_h_last:
+        h_last = torch.empty((batch, nheads, headdim, d_state), dtype=torch.float32, device=x.device)
+    rc = load_library().ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                    _ptr(y), _ptr(h_last), batch, seqlen, nheads, headdim, ngroups, d_state,
+                                    _io_dtype(x), flags, _ptr(dt_bias), _stream(stream))
+    if rc != SSM_OK:
+        raise SsmError(rc, "ssm_ssd_fwd")
+    return y, h_last
 
 
 def ssm_conv1d_fwd(x, w, bias=None, state_in=None, *, y=None, state_out=None, want_state=True, silu=True,

@@ -376,6 +376,46 @@ int bwd_impl(const void* x, const void* delta, const float* A, const void* B, co
   return ssm::launch_scan_bwd(p, lay, plan) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+int ssd_impl(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+             const void* z, const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen, int64_t nheads,
+             int64_t headdim, int64_t ngroups, int64_t d_state, int32_t io_dtype, uint32_t flags,
+             const float* dt_bias, void* stream) {
+  if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0 || ngroups <= 0 || d_state <= 0) return SSM_ERR_BAD_DIM;
+  if (seqlen > kMaxSeqlen || nheads > (1 << 20)) return SSM_ERR_BAD_DIM;
+  if (io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
+  if (headdim != 64 || (d_state != 64 && d_state != 128) || nheads % ngroups != 0) return SSM_ERR_UNSUPPORTED;
+  if (flags & ~(uint32_t)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
+  if (!(flags & SSM_FLAG_DELTA_SOFTPLUS)) dt_bias = nullptr;
+  int64_t n_io, n_dt, n_bc, n_h;
+  if (!mul3(batch, seqlen, nheads * headdim, &n_io) || !mul3(batch, seqlen, nheads, &n_dt) ||
+      !mul3(batch, seqlen, ngroups * d_state, &n_bc) || !mul3(batch, nheads * headdim, d_state, &n_h))
+    return SSM_ERR_BAD_DIM;
+  if (n_io > INT64_MAX / 4 || n_bc > INT64_MAX / 4 || n_h > INT64_MAX / 8) return SSM_ERR_BAD_DIM;
+  const int64_t b_io = n_io * 2, b_dt = n_dt * 2, b_bc = n_bc * 2, b_h = n_h * 4, b_p = nheads * 4;
+  if (n_io > 0 && (x == nullptr || dt == nullptr || y == nullptr || B == nullptr || C == nullptr || A == nullptr))
+    return SSM_ERR_NULL_ARG;
+  if ((flags & SSM_FLAG_DELTA_SOFTPLUS) && nheads > 0 && dt_bias == nullptr) return SSM_ERR_NULL_ARG;
+  if (!aligned(x, 16) || !aligned(z, 16) || !aligned(y, 16) || !aligned(B, 16) || !aligned(C, 16) ||
+      !aligned(dt, 2) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) || !aligned(h_last, 4) ||
+      !aligned(dt_bias, 4))
+    return SSM_ERR_MISALIGNED;
+  const void* ins[] = {x, dt, A, B, C, D, z, h0, dt_bias};
+  const int64_t inb[] = {b_io, b_dt, b_p, b_bc, b_bc, D ? b_p : 0, z ? b_io : 0, h0 ? b_h : 0, dt_bias ? b_p : 0};
+  for (int k = 0; k < 9; ++k)
+    if (overlap(y, b_io, ins[k], inb[k])) return SSM_ERR_ALIAS;
+  if (h_last != nullptr) {
+    for (int k = 0; k < 7; ++k)
+      if (overlap(h_last, b_h, ins[k], inb[k])) return SSM_ERR_ALIAS;
+    if (overlap(h_last, b_h, y, b_io) || overlap(h_last, b_h, dt_bias, dt_bias ? b_p : 0)) return SSM_ERR_ALIAS;
+    if (h0 != nullptr && h0 != h_last && overlap(h_last, b_h, h0, b_h)) return SSM_ERR_ALIAS;
+  }
+  if (batch * nheads > INT32_MAX) return SSM_ERR_BAD_DIM;
+  if (batch == 0 || nheads == 0) return SSM_OK;
+  ssm::SsdLaunch p{x, dt, A, B, C, D, z, h0, y, h_last, dt_bias, flags, batch, seqlen, nheads, ngroups,
+                   (int32_t)d_state, static_cast<hipStream_t>(stream)};
+  return ssm::launch_ssd(p) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 int conv_impl(const void* x, const float* w, const float* bias, const float* state_in, void* y, float* state_out,
               int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_conv, int32_t io_dtype, int32_t apply_silu,
               void* stream, bool update) {
@@ -457,6 +497,14 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
                  int32_t io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, ckpt, dx, ddelta, dA, dB, dC, dD, dz, dh0, d_dt_bias,
                   batch, seqlen, d_inner, d_state, io_dtype, flags, workspace, workspace_bytes, stream);
+}
+
+int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                const void* z, const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen,
+                int64_t nheads, int64_t headdim, int64_t ngroups, int64_t d_state, int32_t io_dtype, uint32_t flags,
+                const float* dt_bias, void* stream) {
+  return ssd_impl(x, dt, A, B, C, D, z, h0, y, h_last, batch, seqlen, nheads, headdim, ngroups, d_state, io_dtype,
+                  flags, dt_bias, stream);
 }
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }

@@ -152,6 +152,27 @@ BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, in
                                   const BwdPlan& plan, int64_t* total_floats);
 hipError_t launch_scan_bwd(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPlan& pl);
 
+// Scan with a scalar decay per head (Mamba-2 / SSD form).  bf16 io (x, dt,
+// B, C, z, y), fp32 A, D, dt_bias, h0, h_last; headdim 64.
+struct SsdLaunch {
+  const void* x;      // [batch][seqlen][nheads][64]
+  const void* dt;     // [batch][seqlen][nheads]
+  const float* A;     // [nheads]
+  const void* B;      // [batch][seqlen][ngroups][d_state]
+  const void* C;
+  const float* D;     // nullable
+  const void* z;      // nullable
+  const float* h0;    // nullable, [batch][nheads][64][d_state]
+  void* y;
+  float* h_last;      // nullable
+  const float* dt_bias;  // used with SSM_FLAG_DELTA_SOFTPLUS
+  uint32_t flags;
+  int64_t batch, seqlen, nheads, ngroups;
+  int32_t d_state;
+  hipStream_t stream;
+};
+hipError_t launch_ssd(const SsdLaunch& p);
+
 hipError_t launch_scan(const ScanLaunch& p);
 template <int MODE>
 hipError_t launch_scan_mode(const ScanLaunch& p);  // one translation unit per MODE

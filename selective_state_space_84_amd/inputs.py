@@ -77,6 +77,24 @@ DECODE = DecodeConfig("decode-256x5120", 256, 5120, 16, "bf16", 1000, 4)
 SCAN_CONFIGS = {c.name: c for c in (TINY, MAMBA_130M, MAMBA_1P4B, MAMBA_2P8B_LONG)}
 
 
+@dataclass(frozen=True)
+class SsdConfig:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    d_state: int
+    seed: int
+
+
+# Scan with a scalar decay per head: a Mamba-2 layer of the 2.7B shape
+# (d_model 2560, expand 2 -> 5120 channels = 80 heads of 64, d_state 128, one
+# group of B/C).
+SSD_2P7B = SsdConfig("mamba2-2.7b-layer", 8, 4096, 80, 64, 1, 128, 5)
+
+
 def round_to_f32(a: np.ndarray) -> np.ndarray:
     return np.asarray(a, dtype=np.float64).astype(np.float32)
 
@@ -246,6 +264,51 @@ def make_scan_grads(batch: int, seqlen: int, d_inner: int, d_state: int, dtype: 
             fill(k)
     dh = round_to_f32(np.random.default_rng(dh_kid).standard_normal((batch, d_inner, d_state)))
     return {"dy": dy, "dh_last": dh}
+
+
+def make_ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, ngroups: int, d_state: int, seed: int,
+                    nonzero_h0: bool = False, raw_dt: bool = False,
+                    threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Host tensors for the scan with a scalar decay per head (bf16 io).
+
+    x, z: (batch, seqlen, nheads, headdim) ~ N(0,1); dt: (batch, seqlen,
+    nheads) = softplus(0.5*N(0,1) + inv_softplus(U[1e-3, 1e-1]_h)) (with
+    ``raw_dt`` the raw 0.5*N(0,1) and dt_bias = inv_softplus(U)); B, C:
+    (batch, seqlen, ngroups, d_state) ~ N(0,1); A_h = -U[1, 16]; D = 1; h0 ~
+    N(0, 0.1^2) if requested.  Per-row streams, like the other generators.
+    """
+    kids = np.random.SeedSequence([seed, 0x55D]).spawn(8)
+    r = np.random.default_rng(kids[0])
+    u = r.uniform(1e-3, 1e-1, size=nheads)
+    inv_sp = _inv_softplus(u)
+    A = -(1.0 + 15.0 * np.random.default_rng(kids[1]).uniform(size=nheads))
+    out = {"x": np.empty((batch, seqlen, nheads, headdim), np.uint16),
+           "z": np.empty((batch, seqlen, nheads, headdim), np.uint16),
+           "dt": np.empty((batch, seqlen, nheads), np.uint16),
+           "B": np.empty((batch, seqlen, ngroups, d_state), np.uint16),
+           "C": np.empty((batch, seqlen, ngroups, d_state), np.uint16)}
+    grand = {k: kids[2 + i].spawn(batch) for i, k in enumerate(("x", "z", "dt", "B", "C"))}
+
+    def fill(b: int):
+        for k in ("x", "z"):
+            out[k][b] = _to_io(np.random.default_rng(grand[k][b]).standard_normal((seqlen, nheads, headdim)), "bf16")
+        noise = 0.5 * np.random.default_rng(grand["dt"][b]).standard_normal((seqlen, nheads))
+        out["dt"][b] = _to_io(noise if raw_dt else _softplus(noise + inv_sp[None, :]), "bf16")
+        for k in ("B", "C"):
+            out[k][b] = _to_io(np.random.default_rng(grand[k][b]).standard_normal((seqlen, ngroups, d_state)), "bf16")
+
+    if batch > 1 and batch * seqlen * nheads * headdim > (1 << 20):
+        with ThreadPoolExecutor(_threads(threads)) as ex:
+            list(ex.map(fill, range(batch)))
+    else:
+        for b in range(batch):
+            fill(b)
+    out["A"] = round_to_f32(A)
+    out["D"] = np.ones(nheads, dtype=np.float32)
+    out["dt_bias"] = round_to_f32(inv_sp) if raw_dt else round_to_f32(u)
+    out["h0"] = (round_to_f32(0.1 * np.random.default_rng(kids[7]).standard_normal((batch, nheads, headdim, d_state)))
+                 if nonzero_h0 else None)
+    return out
 
 
 def decode_inputs(cfg: DecodeConfig, steps: Optional[int] = None, threads: Optional[int] = None):

@@ -230,3 +230,30 @@ def test_bwd_argument_errors(lib):
     need = lib.ssm_scan_bwd_workspace_size(2, 4, 8, 16)
     assert _bwd(lib, ws_bytes=need - 4) == bd.SSM_ERR_WORKSPACE
     assert _bwd(lib, ws=P0 + 64 * MB + 16) == bd.SSM_ERR_MISALIGNED
+
+
+def _ssd(lib, x=P0, dt=P0 + MB, A=P0 + 2 * MB, B=P0 + 3 * MB, C=P0 + 4 * MB, D=None, z=None, h0=None,
+         y=P0 + 8 * MB, h_last=None, batch=2, L=70, H=4, P=64, G=1, N=128, dtype=1, flags=0, dt_bias=None):
+    return lib.ssm_ssd_fwd(x, dt, A, B, C, D, z, h0, y, h_last, batch, L, H, P, G, N, dtype, flags, dt_bias, None)
+
+
+def test_ssd_argument_errors(lib):
+    assert _ssd(lib, x=None) == bd.SSM_ERR_NULL_ARG
+    assert _ssd(lib, dt=None) == bd.SSM_ERR_NULL_ARG
+    assert _ssd(lib, y=None) == bd.SSM_ERR_NULL_ARG
+    assert _ssd(lib, flags=bd.SSM_FLAG_DELTA_SOFTPLUS) == bd.SSM_ERR_NULL_ARG
+    assert _ssd(lib, batch=-1) == bd.SSM_ERR_BAD_DIM
+    assert _ssd(lib, G=0) == bd.SSM_ERR_BAD_DIM
+    # bf16 io, headdim 64, d_state 64 or 128, heads a multiple of groups, known flags only.
+    assert _ssd(lib, dtype=0) == bd.SSM_ERR_UNSUPPORTED
+    assert _ssd(lib, P=32) == bd.SSM_ERR_UNSUPPORTED
+    assert _ssd(lib, N=16) == bd.SSM_ERR_UNSUPPORTED
+    assert _ssd(lib, H=4, G=3) == bd.SSM_ERR_UNSUPPORTED
+    assert _ssd(lib, flags=bd.SSM_FLAG_EXACT_ZOH) == bd.SSM_ERR_UNSUPPORTED
+    # 16-byte alignment for the vector-loaded tensors.
+    assert _ssd(lib, x=P0 + 8) == bd.SSM_ERR_MISALIGNED
+    assert _ssd(lib, B=P0 + 3 * MB + 4) == bd.SSM_ERR_MISALIGNED
+    assert _ssd(lib, dt=P0 + MB + 1) == bd.SSM_ERR_MISALIGNED
+    # y over an input; h_last over x.
+    assert _ssd(lib, y=P0 + 64) == bd.SSM_ERR_ALIAS
+    assert _ssd(lib, h_last=P0 + 128) == bd.SSM_ERR_ALIAS
