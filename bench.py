@@ -284,12 +284,14 @@ def bench_ssd(steps, dev):
     el = cfg.batch * cfg.seqlen * cfg.nheads * cfg.headdim
     alg = (3 * el * 2 + cfg.batch * cfg.seqlen * cfg.nheads * 2 + 2 * cfg.batch * cfg.seqlen * cfg.ngroups * cfg.d_state * 2
            + 2 * cfg.nheads * 4 + cfg.batch * cfg.nheads * cfg.headdim * cfg.d_state * 4)
-    # Matrix-core work as issued per 64-step chunk and (row, head): scores 10
-    # causal 16x16 tiles x N/32 steps; masked scores x X and C x H_prev and
-    # the state update with hi/lo operand pairs; 16x16x32 products.
+    # Matrix-core work as issued per 32-step chunk and (row, head): three
+    # causal 16x16 score tiles over N/32 slices, then per 16-channel wave the
+    # two output tiles (masked scores x X with hi/lo scores, C x H with hi/lo
+    # state over N/32 slices) and N/16 state tiles (hi/lo scaled input);
+    # 16x16x32 products.
     nk = cfg.d_state // 32
-    mfma = 10 * nk + 48 + 4 * 4 * nk * 2 + 4 * (cfg.d_state // 16) * 2 * 2
-    flops = mfma * 16 * 16 * 32 * 2 * (-(-cfg.seqlen // 64)) * cfg.batch * cfg.nheads
+    mfma = 3 * nk + 4 * (2 * (2 + 2 * nk) + 2 * (cfg.d_state // 16))
+    flops = mfma * 16 * 16 * 32 * 2 * (-(-cfg.seqlen // 32)) * cfg.batch * cfg.nheads
     gbps = alg / (ms * 1e-3) / 1e9
     return {"workload": "%s ssd (batch %d, L %d, %d heads x %d, d_state %d, bf16 io)" % (
                 cfg.name, cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.d_state),
