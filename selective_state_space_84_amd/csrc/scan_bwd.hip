@@ -65,27 +65,9 @@ __device__ __forceinline__ void chunk_blocks(const BwdDims& dm, int c, int& kb, 
 
 __device__ __forceinline__ float sigmoid(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
 
-// A wave-uniform pointer re-read through readfirstlane: the compiler then
-// treats it as an opaque SGPR value.  Row pointers that move by a fixed
-// amount per block are passed through this so that loop strength reduction
-// does not turn "SGPR base + 32-bit lane offset" into one 64-bit per-lane
-// pointer per tensor and step (which would hold ~100 VGPRs).
-// The result is typed as a global-memory pointer, so loads and stores
-// through it stay global (SGPR base + VGPR offset) instead of flat.
-typedef char __attribute__((address_space(1))) gchar;
-__device__ __forceinline__ gchar* uniform_ptr(const void* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<gchar*>(((uint64_t)hi << 32) | lo);
-}
 template <typename T>
 __device__ __forceinline__ float gld(const gchar* base, uint32_t off) {
   return io_to_f32(*reinterpret_cast<const T __attribute__((address_space(1)))*>(base + off));
-}
-template <typename T>
-__device__ __forceinline__ T gldr(const gchar* base, uint32_t off) {
-  return *reinterpret_cast<const T __attribute__((address_space(1)))*>(base + off);
 }
 template <typename T>
 __device__ __forceinline__ void gst(gchar* base, uint32_t off, float v) {

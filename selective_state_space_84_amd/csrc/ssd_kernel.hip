@@ -80,13 +80,24 @@ __device__ __forceinline__ u16x4 lds_tr4(const uint16_t* p) {
                             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s16x4*)const_cast<uint16_t*>(p)));
 }
 
-__device__ __forceinline__ uint16_t to_bf16(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
-__device__ __forceinline__ float from_bf16(uint16_t v) { return __builtin_bit_cast(float, (uint32_t)v << 16); }
-__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
-  hi = to_bf16(v);
-  lo = to_bf16(v - from_bf16(hi));
-}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Two floats to a packed bf16 pair (round to nearest even, one instruction).
+__device__ __forceinline__ uint32_t pack_bf16(float v0, float v1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v0, v1}, bf16x2));
+}
+__device__ __forceinline__ float lo_f32(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t v) { return __builtin_bit_cast(float, v & 0xffff0000u); }
+// v0, v1 = hi + lo to about 16 significant bits, as packed bf16 pairs
+// (.x = hi, .y = lo).
+__device__ __forceinline__ uint2 split2(float v0, float v1) {
+  const uint32_t hi = pack_bf16(v0, v1);
+  return make_uint2(hi, pack_bf16(v0 - lo_f32(hi), v1 - hi_f32(hi)));
+}
+__device__ __forceinline__ u16x8 as_u16x8(const u32x4& v) { return __builtin_bit_cast(u16x8, v); }
 __device__ __forceinline__ u16x8 cat(const u16x4& a, const u16x4& b) {
   return u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
@@ -95,6 +106,7 @@ __device__ __forceinline__ u16x8 cat(const u16x4& a, const u16x4& b) {
 // C tile: the order in which the state accumulators hold the states.
 __device__ __forceinline__ int cperm(int o) { return o < 16 ? 2 * o : 2 * (o - 16) + 4; }
 
+// MODE bit 0: dt is softplus(dt + dt_bias); bit 1: gate with silu(z).
 template <int N, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))  // all (row, head) groups resident
 k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const float* __restrict__ A,
@@ -106,6 +118,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   constexpr int SB = N + 16;            // B tile row stride: transposing reads conflict-free
   constexpr int SC = N + 8;             // C tile row stride: 16-byte reads conflict-free
   constexpr int PB = kQ * N / 8 / 256;  // 16-byte pieces of B (and of C) per thread
+  constexpr bool kGate = (MODE & 2) != 0;
   __shared__ __align__(16) uint16_t sX[kQ * kSX];
   __shared__ __align__(16) uint16_t sB[2][kQ * SB];
   __shared__ __align__(16) uint16_t sC[2][kQ * SC];
@@ -121,11 +134,11 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   const int64_t b = bid / dm.nheads;
   const int g = h / (dm.nheads / dm.ngroups);
   const int64_t L = dm.seqlen;
-  const int64_t HP = (int64_t)dm.nheads * kHP;
+  const uint32_t rowb = (uint32_t)dm.nheads * kHP * 2;    // bytes per step of x, z, y
+  const uint32_t growb = (uint32_t)dm.ngroups * N * 2;    // bytes per step of B, C
   const float Al2 = A[h] * kLog2e;
   const float Dh = D != nullptr ? D[h] : 0.f;
   const float dtb = (MODE & 1) ? dt_bias[h] : 0.f;
-  const bool has_z = z != nullptr;
   float* const lv = &sv[w][0][0];
   float* const dv = &sv[w][1][0];
   float* const wv = &sv[w][2][0];
@@ -140,25 +153,43 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
 #pragma unroll
       for (int j = 0; j < 4; ++j) accH[nt][j] = hp != nullptr ? hp[16 * nt + j] : 0.f;
   }
+  // Scores with k < 16 <= i are never written: zero them once.
+  if (tid < 64) {
+    const int k = tid >> 2, i = 16 + 4 * (tid & 3);
+    *reinterpret_cast<u16x4*>(&sW[0][k * kSW + i]) = u16x4{0, 0, 0, 0};
+    *reinterpret_cast<u16x4*>(&sW[1][k * kSW + i]) = u16x4{0, 0, 0, 0};
+  }
 
-  // Staging registers, one chunk ahead.
+  // Staging registers, one chunk ahead.  Rows past the end of the sequence
+  // repeat the last row: they only ever meet zero weights (dt = 0 there)
+  // or feed outputs that are not stored.
   const int sx_t = tid >> 3, sx_c = (tid & 7) * 8;
   u16x8 rx, rb[PB], rc[PB];
+  u32x2 rz[2];
   uint16_t rdt = 0;
   auto fetch = [&](int64_t c) {
     const int64_t t0 = c * kQ;
-    const int nt_ = (int)min((int64_t)kQ, L - t0);
-    const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
-    rx = sx_t < nt_ ? *reinterpret_cast<const u16x8*>(x + (b * L + t0 + sx_t) * HP + (int64_t)h * kHP + sx_c) : zero;
+    const int last = (int)min((int64_t)kQ, L - t0) - 1;
+    const gchar* xb = uniform_ptr(x + ((b * L + t0) * dm.nheads + h) * kHP);
+    rx = gldr<u16x8>(xb, (uint32_t)min(sx_t, last) * rowb + sx_c * 2);
+    const gchar* bb = uniform_ptr(B + ((b * L + t0) * dm.ngroups + g) * N);
+    const gchar* cb = uniform_ptr(C + ((b * L + t0) * dm.ngroups + g) * N);
 #pragma unroll
     for (int r = 0; r < PB; ++r) {
       const int piece = tid + 256 * r;
       const int t = piece / (N / 8), n8 = (piece % (N / 8)) * 8;
-      const int64_t o = ((b * L + t0 + t) * dm.ngroups + g) * N + n8;
-      rb[r] = t < nt_ ? *reinterpret_cast<const u16x8*>(B + o) : zero;
-      rc[r] = t < nt_ ? *reinterpret_cast<const u16x8*>(C + o) : zero;
+      const uint32_t o = (uint32_t)min(t, last) * growb + n8 * 2;
+      rb[r] = gldr<u16x8>(bb, o);
+      rc[r] = gldr<u16x8>(cb, o);
     }
-    rdt = lane < nt_ ? dt[(b * L + t0 + lane) * dm.nheads + h] : (uint16_t)0;
+    const gchar* db = uniform_ptr(dt + (b * L + t0) * dm.nheads + h);
+    rdt = gldr<uint16_t>(db, (uint32_t)min(lane, last) * (uint32_t)dm.nheads * 2);
+    if (kGate) {
+      // Gate inputs in the Y^T layout: rows 16 kt + r16, channels 16w + 4q4 .. +3.
+      const gchar* zb = uniform_ptr(z + ((b * L + t0) * dm.nheads + h) * kHP + 16 * w);
+      rz[0] = gldr<u32x2>(zb, (uint32_t)min(r16, last) * rowb + 8 * q4);
+      rz[1] = gldr<u32x2>(zb, (uint32_t)min(16 + r16, last) * rowb + 8 * q4);
+    }
   };
   auto stage = [&](int buf) {
     *reinterpret_cast<u16x8*>(&sX[sx_t * kSX + sx_c]) = rx;
@@ -181,16 +212,8 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     const int nt_ = (int)min((int64_t)kQ, L - t0);
     stage(buf);
     const uint16_t dcur = rdt;
+    const u32x2 zv[2] = {rz[0], rz[1]};
     if (c + 1 < nchunks) fetch(c + 1);
-    // Gate inputs of this chunk in the Y^T layout: row k = 16 kt + r16, channels 16w + 4q4 .. +3.
-    uint2 zv[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int k = 16 * kt + r16;
-      zv[kt] = make_uint2(0u, 0u);
-      if (has_z && k < nt_)
-        zv[kt] = *reinterpret_cast<const uint2*>(z + (b * L + t0 + k) * HP + (int64_t)h * kHP + 16 * w + 4 * q4);
-    }
     __syncthreads();
 
     // 1. Steps and decay sums (every wave for itself; lane = step).  Steps
@@ -198,7 +221,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     {
       float d = 0.f;
       if (lane < nt_) {
-        d = from_bf16(dcur);
+        d = lo_f32(dcur);
         if (MODE & 1) d = softplus(d + dtb);
       }
       float l = d * Al2;
@@ -234,19 +257,16 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
       const float lk = lv[k];
       const f32x4 li = *reinterpret_cast<const f32x4*>(&lv[16 * it + 4 * q4]);
       const f32x4 di = *reinterpret_cast<const f32x4*>(&dv[16 * it + 4 * q4]);
-      u16x4 hi, lo;
+      float v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 16 * it + 4 * q4 + j;
-        float v = i <= k ? acc[j] * hw_exp2(lk - li[j]) * di[j] : 0.f;
-        if (i == k) v += Dh;
-        uint16_t vh, vl;
-        split_bf16(v, vh, vl);
-        hi[j] = vh;
-        lo[j] = vl;
+        v[j] = i <= k ? acc[j] * hw_exp2(lk - li[j]) * di[j] : 0.f;
+        if (i == k) v[j] += Dh;
       }
-      *reinterpret_cast<u16x4*>(&sW[0][k * kSW + 16 * it + 4 * q4]) = hi;
-      *reinterpret_cast<u16x4*>(&sW[1][k * kSW + 16 * it + 4 * q4]) = lo;
+      const uint2 s01 = split2(v[0], v[1]), s23 = split2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(&sW[0][k * kSW + 16 * it + 4 * q4]) = make_uint2(s01.x, s23.x);
+      *reinterpret_cast<uint2*>(&sW[1][k * kSW + 16 * it + 4 * q4]) = make_uint2(s01.y, s23.y);
     }
     // 3. This wave's x columns over the chunk's steps: lane (r16, q4) gets
     //    x[8 q4 + j][16 w + r16], j < 8.
@@ -257,23 +277,24 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     // 4. Y^T = X^T W^T + (H^T C^T) diag(exp(l)); gate; store.
     u16x8 hhi[NK], hlo[NK];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
+    for (int kk = 0; kk < NK; ++kk) {
+      u32x4 vh, vl;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint16_t vh, vl;
-        split_bf16(accH[2 * kk + (j >> 2)][j & 3], vh, vl);
-        hhi[kk][j] = vh;
-        hlo[kk][j] = vl;
+      for (int q = 0; q < 4; ++q) {
+        const f32x4& a = accH[2 * kk + (q >> 1)];
+        const uint2 sp = split2(a[2 * (q & 1)], a[2 * (q & 1) + 1]);
+        vh[q] = sp.x;
+        vl[q] = sp.y;
       }
+      hhi[kk] = as_u16x8(vh);
+      hlo[kk] = as_u16x8(vl);
+    }
+    gchar* yb = uniform_ptr(y + ((b * L + t0) * dm.nheads + h) * kHP + 16 * w);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int k = 16 * kt + r16;
-      const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
-      const bool upper = kt == 0 && q4 >= 2;  // steps i >= 16 > k
-      u16x8 whi = *reinterpret_cast<const u16x8*>(&sW[0][k * kSW + 8 * q4]);
-      u16x8 wlo = *reinterpret_cast<const u16x8*>(&sW[1][k * kSW + 8 * q4]);
-      whi = upper ? zero : whi;
-      wlo = upper ? zero : wlo;
+      const u16x8 whi = *reinterpret_cast<const u16x8*>(&sW[0][k * kSW + 8 * q4]);
+      const u16x8 wlo = *reinterpret_cast<const u16x8*>(&sW[1][k * kSW + 8 * q4]);
       f32x4 accY = {0.f, 0.f, 0.f, 0.f};
       accY = mma(xt, whi, accY);
       accY = mma(xt, wlo, accY);
@@ -285,19 +306,18 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
         accO = mma(hlo[kk], cb, accO);
       }
       const float ek = ev[k];
-      if (k < nt_) {
-        u16x4 out;
+      float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float v = accY[j] + ek * accO[j];
-          if (has_z) {
-            const uint32_t zw = j < 2 ? zv[kt].x : zv[kt].y;
-            v *= silu(from_bf16((uint16_t)((j & 1) ? zw >> 16 : zw & 0xffffu)));
-          }
-          out[j] = to_bf16(v);
-        }
-        *reinterpret_cast<u16x4*>(y + (b * L + t0 + k) * HP + (int64_t)h * kHP + 16 * w + 4 * q4) = out;
+      for (int j = 0; j < 4; ++j) v[j] = accY[j] + ek * accO[j];
+      if (kGate) {
+        const u32x2 zz = zv[kt];
+        v[0] *= silu(lo_f32(zz.x));
+        v[1] *= silu(hi_f32(zz.x));
+        v[2] *= silu(lo_f32(zz.y));
+        v[3] *= silu(hi_f32(zz.y));
       }
+      // Row k of this wave's channels 16w + 4q4 .. +3 (8 bytes).
+      if (k < nt_) gstr<u32x2>(yb, (uint32_t)k * rowb + 8 * q4, u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
     }
 
     // 5. State: H = exp(l_Q) H + B^T (w o X).
@@ -305,13 +325,17 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     {
       const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wv[8 * q4]);
       const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wv[8 * q4 + 4]);
+      const u32x4 xd = __builtin_bit_cast(u32x4, xt);
+      u32x4 vh, vl;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint16_t vh, vl;
-        split_bf16((j < 4 ? w0[j] : w1[j - 4]) * from_bf16(xt[j]), vh, vl);
-        xwh[j] = vh;
-        xwl[j] = vl;
+      for (int q = 0; q < 4; ++q) {
+        const float wa = q < 2 ? w0[2 * q] : w1[2 * q - 4], wb = q < 2 ? w0[2 * q + 1] : w1[2 * q - 3];
+        const uint2 sp = split2(wa * lo_f32(xd[q]), wb * hi_f32(xd[q]));
+        vh[q] = sp.x;
+        vl[q] = sp.y;
       }
+      xwh = as_u16x8(vh);
+      xwl = as_u16x8(vl);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -343,7 +367,9 @@ hipError_t launch_ssd_n(const SsdLaunch& p) {
                   static_cast<const uint16_t*>(p.C), p.D, static_cast<const uint16_t*>(p.z), p.h0,
                   static_cast<uint16_t*>(p.y), p.h_last, p.dt_bias, dm);
   };
-  return (p.flags & 1u) ? go(k_ssd_fwd<N, 1>) : go(k_ssd_fwd<N, 0>);
+  const bool sp = (p.flags & 1u) != 0, gate = p.z != nullptr;
+  if (gate) return sp ? go(k_ssd_fwd<N, 3>) : go(k_ssd_fwd<N, 2>);
+  return sp ? go(k_ssd_fwd<N, 1>) : go(k_ssd_fwd<N, 0>);
 }
 
 }  // namespace
