@@ -47,10 +47,20 @@ def bwd_slots_per_element(d_state: int) -> int:
     return 16 * d_state + 30
 
 
-def _kernel_source_sha() -> str:
+# Sources each kernel family is built from; a traffic figure is reported only
+# while the sources of its own kernel still match the ones it was taken on.
+_KERNEL_SOURCES = {
+    "scan": ("scan_sweep.h", "scan_mode0.hip", "scan_aux.hip"),
+    "decode": ("update_kernel.hip",),
+    "conv": ("conv_kernels.hip",),
+    "bwd": ("scan_bwd.hip", "scan_sweep.h"),
+    "ssd": ("ssd_kernel.hip",),
+}
+
+
+def _kernel_source_sha(kind: str) -> str:
     h = hashlib.sha256()
-    for f in ("scan_sweep.h", "scan_mode0.hip", "scan_aux.hip", "update_kernel.hip", "conv_kernels.hip",
-              "scan_bwd.hip", "ssd_kernel.hip", "ssm_device.h", "ssm_internal.h"):
+    for f in _KERNEL_SOURCES[kind] + ("ssm_device.h", "ssm_internal.h"):
         with open(os.path.join(REPO, "selective_state_space_84_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -165,7 +175,7 @@ def bench_decode(steps, dev):
         "achieved_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "frac_of_8tbs": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "input_gen_s": round(gen_s, 1),
-        "traffic_bytes_per_step": _traffic(cfg.name, _kernel_source_sha()),
+        "traffic_bytes_per_step": _traffic(cfg.name, _kernel_source_sha("decode")),
         "note": "time per step includes launch gaps between 1000 back-to-back eager launches; "
                 "the 84 MB state can stay resident in the 256 MB Infinity Cache between steps",
     }
@@ -297,7 +307,8 @@ def bench_ssd(steps, dev):
                 cfg.name, cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.d_state),
             "steps": steps, "ms_per_step": round(ms, 6), "elements_per_s": round(el / (ms * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": alg},
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": alg,
+                         "traffic": _traffic(cfg.name, _kernel_source_sha("ssd"))},
             "mfma": {"tflops_issued": round(flops / (ms * 1e-3) / 1e12, 2), "peak_bf16_tflops": 2500.0},
             "input_gen_s": round(gen_s, 1)}
 
@@ -386,7 +397,7 @@ def main():
     gbps = alg_bytes / (ms * 1e-3) / 1e9
     slots = scan_slots_per_element(cfg.d_state)
     achieved_slots = el_per_s * slots / 1e12
-    sha = _kernel_source_sha()
+    sha = _kernel_source_sha("scan")
     out = {
         "metric": "selective-scan elements/s (B·L·d_inner) and achieved HBM GB/s vs peak",
         "value": round(el_per_s, 1),
