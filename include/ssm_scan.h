@@ -294,7 +294,7 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
  *               written); h_last may be the h0 buffer
  *   io_dtype  : SSM_DTYPE_BF16 only; headdim: 64; d_state: 64 or 128;
  *   nheads a multiple of ngroups.  Other values: SSM_ERR_UNSUPPORTED.
- *   nheads above 65536 or seqlen above the scan's limit: SSM_ERR_BAD_DIM.
+ *   nheads above 32768 or seqlen above the scan's limit: SSM_ERR_BAD_DIM.
  * No workspace.  Same conventions, validation and error codes as the scan.
  */
 int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,

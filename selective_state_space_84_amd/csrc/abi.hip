@@ -381,9 +381,9 @@ int ssd_impl(const void* x, const void* dt, const float* A, const void* B, const
              int64_t headdim, int64_t ngroups, int64_t d_state, int32_t io_dtype, uint32_t flags,
              const float* dt_bias, void* stream) {
   if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0 || ngroups <= 0 || d_state <= 0) return SSM_ERR_BAD_DIM;
-  // The kernel addresses a 32-step chunk with 32-bit byte offsets: 65536
-  // heads of 64 channels (or groups of 128 states) keep them below 2^32.
-  if (seqlen > kMaxSeqlen || nheads > (1 << 16)) return SSM_ERR_BAD_DIM;
+  // The kernel addresses a 32-step chunk with 24-bit row multiplies: 32768
+  // heads of 64 channels (or groups of 128 states) keep a step below 2^24 bytes.
+  if (seqlen > kMaxSeqlen || nheads > (1 << 15)) return SSM_ERR_BAD_DIM;
   if (io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
   if (headdim != 64 || (d_state != 64 && d_state != 128) || nheads % ngroups != 0) return SSM_ERR_UNSUPPORTED;
   if (flags & ~(uint32_t)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;

@@ -102,6 +102,21 @@ __device__ __forceinline__ u16x8 cat(const u16x4& a, const u16x4& b) {
   return u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Inclusive prefix sum over lanes 0..31 (lanes 32..63 hold a second,
+// unused scan).  DPP row shifts add within each row of 16 lanes (lanes whose
+// source falls outside the row read 0), then row 0's total (lane 15) is
+// broadcast into row 1: all on the VALU, no LDS round trips.
+__device__ __forceinline__ float scan32(float v) {
+  int x = __builtin_bit_cast(int, v);
+  x = __builtin_bit_cast(int, __builtin_bit_cast(float, x) + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true)));
+  x = __builtin_bit_cast(int, __builtin_bit_cast(float, x) + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true)));
+  x = __builtin_bit_cast(int, __builtin_bit_cast(float, x) + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true)));
+  x = __builtin_bit_cast(int, __builtin_bit_cast(float, x) + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true)));
+  // row_bcast:15 into rows 1 and 3 only (row mask 0b1010); other rows add 0.
+  x = __builtin_bit_cast(int, __builtin_bit_cast(float, x) + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false)));
+  return __builtin_bit_cast(float, x);
+}
+
 // Position of state column o (0..31 inside a 32-wide slice) in the permuted
 // C tile: the order in which the state accumulators hold the states.
 __device__ __forceinline__ int cperm(int o) { return o < 16 ? 2 * o : 2 * (o - 16) + 4; }
@@ -115,12 +130,15 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
           float* __restrict__ h_last, const float* __restrict__ dt_bias, const SsdDims dm) {
   constexpr int NT = N / 16;            // state tiles of 16
   constexpr int NK = N / 32;            // contraction slices over the state
-  constexpr int SB = N + 16;            // B tile row stride: transposing reads conflict-free
-  constexpr int SC = N + 8;             // C tile row stride: 16-byte reads conflict-free
-  constexpr int PB = kQ * N / 8 / 256;  // 16-byte pieces of B (and of C) per thread
+  constexpr int SC = N + 8;             // B and C tile row stride: 16-byte reads conflict-free
+  constexpr int PB = kQ * N / 8 / 256;  // 16-byte pieces of C per thread
+  constexpr int GT = 4 * kQ + 8;        // transposed B: groups of 4 state rows of kQ steps, padded
+  constexpr int NQ = N / 4;             // 4-state column groups of B
+  constexpr int BT = NQ * (kQ / 4);     // threads that stage B (4 steps x 4 states each)
   constexpr bool kGate = (MODE & 2) != 0;
   __shared__ __align__(16) uint16_t sX[kQ * kSX];
-  __shared__ __align__(16) uint16_t sB[2][kQ * SB];
+  __shared__ __align__(16) uint16_t sBp[kQ * SC];      // B rows, states in the permuted order (scores)
+  __shared__ __align__(16) uint16_t sBt[NQ * GT];      // B^T: (n, t) at (n / 4) GT + (n % 4) kQ + t
   __shared__ __align__(16) uint16_t sC[2][kQ * SC];
   __shared__ __align__(16) uint16_t sW[2][kQ * kSW];  // masked scores [k][i], hi and lo planes
   __shared__ __align__(16) float sv[4][4][kQ];         // per wave: l (log2 units), dt, w, exp(l)
@@ -134,8 +152,10 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   const int64_t b = bid / dm.nheads;
   const int g = h / (dm.nheads / dm.ngroups);
   const int64_t L = dm.seqlen;
-  const uint32_t rowb = (uint32_t)dm.nheads * kHP * 2;    // bytes per step of x, z, y
-  const uint32_t growb = (uint32_t)dm.ngroups * N * 2;    // bytes per step of B, C
+  // Bytes per step of x, z, y and of B, C: below 2^24 for at most 32768
+  // heads, so row offsets use 24-bit multiplies.
+  const uint32_t rowb = (uint32_t)dm.nheads * kHP * 2;
+  const uint32_t growb = (uint32_t)dm.ngroups * N * 2;
   const float Al2 = A[h] * kLog2e;
   const float Dh = D != nullptr ? D[h] : 0.f;
   const float dtb = (MODE & 1) ? dt_bias[h] : 0.f;
@@ -164,43 +184,67 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   // repeat the last row: they only ever meet zero weights (dt = 0 there)
   // or feed outputs that are not stored.
   const int sx_t = tid >> 3, sx_c = (tid & 7) * 8;
-  u16x8 rx, rb[PB], rc[PB];
+  const int bq = tid % NQ, tq = tid / NQ;  // B: states 4 bq .. +3 of steps 4 tq .. +3
+  u16x8 rx, rc[PB];
+  u32x2 rb[4];
   u32x2 rz[2];
   uint16_t rdt = 0;
   auto fetch = [&](int64_t c) {
     const int64_t t0 = c * kQ;
     const int last = (int)min((int64_t)kQ, L - t0) - 1;
     const gchar* xb = uniform_ptr(x + ((b * L + t0) * dm.nheads + h) * kHP);
-    rx = gldr<u16x8>(xb, (uint32_t)min(sx_t, last) * rowb + sx_c * 2);
+    rx = gldr<u16x8>(xb, __umul24((uint32_t)min(sx_t, last), rowb) + sx_c * 2);
     const gchar* bb = uniform_ptr(B + ((b * L + t0) * dm.ngroups + g) * N);
     const gchar* cb = uniform_ptr(C + ((b * L + t0) * dm.ngroups + g) * N);
 #pragma unroll
     for (int r = 0; r < PB; ++r) {
       const int piece = tid + 256 * r;
       const int t = piece / (N / 8), n8 = (piece % (N / 8)) * 8;
-      const uint32_t o = (uint32_t)min(t, last) * growb + n8 * 2;
-      rb[r] = gldr<u16x8>(bb, o);
-      rc[r] = gldr<u16x8>(cb, o);
+      rc[r] = gldr<u16x8>(cb, __umul24((uint32_t)min(t, last), growb) + n8 * 2);
+    }
+    if (BT == 256 || w < BT / 64) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rb[r] = gldr<u32x2>(bb, __umul24((uint32_t)min(4 * tq + r, last), growb) + 8 * bq);
     }
     const gchar* db = uniform_ptr(dt + (b * L + t0) * dm.nheads + h);
-    rdt = gldr<uint16_t>(db, (uint32_t)min(lane, last) * (uint32_t)dm.nheads * 2);
+    rdt = gldr<uint16_t>(db, __umul24((uint32_t)min(lane, last), (uint32_t)dm.nheads * 2));
     if (kGate) {
       // Gate inputs in the Y^T layout: rows 16 kt + r16, channels 16w + 4q4 .. +3.
       const gchar* zb = uniform_ptr(z + ((b * L + t0) * dm.nheads + h) * kHP + 16 * w);
-      rz[0] = gldr<u32x2>(zb, (uint32_t)min(r16, last) * rowb + 8 * q4);
-      rz[1] = gldr<u32x2>(zb, (uint32_t)min(16 + r16, last) * rowb + 8 * q4);
+      rz[0] = gldr<u32x2>(zb, __umul24((uint32_t)min(r16, last), rowb) + 8 * q4);
+      rz[1] = gldr<u32x2>(zb, __umul24((uint32_t)min(16 + r16, last), rowb) + 8 * q4);
     }
   };
+  // x, C and the row copy of B, before the chunk's first barrier.
   auto stage = [&](int buf) {
     *reinterpret_cast<u16x8*>(&sX[sx_t * kSX + sx_c]) = rx;
+    if (BT == 256 || w < BT / 64) {
+      const int s0 = (4 * bq) & ~31, o = (4 * bq) & 31;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x2*>(&sBp[(4 * tq + r) * SC + s0 + cperm(o)]) = rb[r];
+    }
 #pragma unroll
     for (int r = 0; r < PB; ++r) {
       const int piece = tid + 256 * r;
       const int t = piece / (N / 8), n8 = (piece % (N / 8)) * 8;
-      *reinterpret_cast<u16x8*>(&sB[buf][t * SB + n8]) = rb[r];
       const int s0 = n8 & ~31, o = n8 & 31;
       *reinterpret_cast<u16x4*>(&sC[buf][t * SC + s0 + cperm(o)]) = u16x4{rc[r][0], rc[r][1], rc[r][2], rc[r][3]};
       *reinterpret_cast<u16x4*>(&sC[buf][t * SC + s0 + cperm(o + 4)]) = u16x4{rc[r][4], rc[r][5], rc[r][6], rc[r][7]};
+    }
+  };
+
+  // B^T, after the chunk's first barrier (the previous chunk's state update
+  // is then done with it) and before the second: a 4 x 4 transpose in
+  // registers, one 8-byte write per state.
+  auto stage_bt = [&]() {
+    if (BT == 256 || w < BT / 64) {
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int d = c4 >> 1, sh = (c4 & 1) * 16;
+        const uint32_t t01 = ((rb[0][d] >> sh) & 0xffffu) | (((rb[1][d] >> sh) & 0xffffu) << 16);
+        const uint32_t t23 = ((rb[2][d] >> sh) & 0xffffu) | (((rb[3][d] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<u32x2*>(&sBt[bq * GT + c4 * kQ + 4 * tq]) = u32x2{t01, t23};
+      }
     }
   };
 
@@ -213,8 +257,9 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     stage(buf);
     const uint16_t dcur = rdt;
     const u32x2 zv[2] = {rz[0], rz[1]};
-    if (c + 1 < nchunks) fetch(c + 1);
     __syncthreads();
+    stage_bt();
+    if (c + 1 < nchunks) fetch(c + 1);
 
     // 1. Steps and decay sums (every wave for itself; lane = step).  Steps
     //    past the end count as dt = 0: decay 1, no input.
@@ -224,12 +269,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
         d = lo_f32(dcur);
         if (MODE & 1) d = softplus(d + dtb);
       }
-      float l = d * Al2;
-#pragma unroll
-      for (int off = 1; off < kQ; off <<= 1) {
-        const float o = __shfl_up(l, off, 64);
-        if ((lane & (kQ - 1)) >= off) l += o;
-      }
+      const float l = scan32(d * Al2);
       const float lq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), kQ - 1));
       if (lane < kQ) {
         lv[lane] = l;
@@ -248,8 +288,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const uint16_t* bp = &sB[buf][(16 * it + r16) * SB + 32 * kk + 4 * q4];
-        const u16x8 a = cat(*reinterpret_cast<const u16x4*>(bp), *reinterpret_cast<const u16x4*>(bp + 16));
+        const u16x8 a = *reinterpret_cast<const u16x8*>(&sBp[(16 * it + r16) * SC + 32 * kk + 8 * q4]);
         const u16x8 cb = *reinterpret_cast<const u16x8*>(&sC[buf][(16 * kt + r16) * SC + 32 * kk + 8 * q4]);
         acc = mma(a, cb, acc);
       }
@@ -317,7 +356,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
         v[3] *= silu(hi_f32(zz.y));
       }
       // Row k of this wave's channels 16w + 4q4 .. +3 (8 bytes).
-      if (k < nt_) gstr<u32x2>(yb, (uint32_t)k * rowb + 8 * q4, u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
+      if (k < nt_) gstr<u32x2>(yb, __umul24((uint32_t)k, rowb) + 8 * q4, u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
     }
 
     // 5. State: H = exp(l_Q) H + B^T (w o X).
@@ -339,8 +378,8 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint16_t* bp = &sB[buf][(8 * q4 + (r16 >> 2)) * SB + 16 * nt + 4 * (r16 & 3)];
-      const u16x8 bt = cat(lds_tr4(bp), lds_tr4(bp + 4 * SB));
+      const int n = 16 * nt + r16;
+      const u16x8 bt = *reinterpret_cast<const u16x8*>(&sBt[(n >> 2) * GT + (n & 3) * kQ + 8 * q4]);
       f32x4 acc = accH[nt] * decay;
       acc = mma(bt, xwh, acc);
       acc = mma(bt, xwl, acc);

@@ -244,7 +244,7 @@ def test_ssd_argument_errors(lib):
     assert _ssd(lib, flags=bd.SSM_FLAG_DELTA_SOFTPLUS) == bd.SSM_ERR_NULL_ARG
     assert _ssd(lib, batch=-1) == bd.SSM_ERR_BAD_DIM
     assert _ssd(lib, G=0) == bd.SSM_ERR_BAD_DIM
-    assert _ssd(lib, H=(1 << 16) + 1, G=1) == bd.SSM_ERR_BAD_DIM
+    assert _ssd(lib, H=(1 << 15) + 1, G=1) == bd.SSM_ERR_BAD_DIM
     # bf16 io, headdim 64, d_state 64 or 128, heads a multiple of groups, known flags only.
     assert _ssd(lib, dtype=0) == bd.SSM_ERR_UNSUPPORTED
     assert _ssd(lib, P=32) == bd.SSM_ERR_UNSUPPORTED
