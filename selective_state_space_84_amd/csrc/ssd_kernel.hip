@@ -189,11 +189,27 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   u32x2 rb[4];
   u32x2 rz[2];
   uint16_t rdt = 0;
-  auto fetch = [&](int64_t c) {
+  // The next chunk's rows are requested in two groups, B and C after the
+  // first barrier and x, dt and the gate inputs after the second, so that
+  // the four waves do not put all their loads into the memory pipeline at
+  // once.
+  auto fetch_xz = [&](int64_t c) {
     const int64_t t0 = c * kQ;
     const int last = (int)min((int64_t)kQ, L - t0) - 1;
     const gchar* xb = uniform_ptr(x + ((b * L + t0) * dm.nheads + h) * kHP);
     rx = gldr<u16x8>(xb, __umul24((uint32_t)min(sx_t, last), rowb) + sx_c * 2);
+    const gchar* db = uniform_ptr(dt + (b * L + t0) * dm.nheads + h);
+    rdt = gldr<uint16_t>(db, __umul24((uint32_t)min(lane, last), (uint32_t)dm.nheads * 2));
+    if (kGate) {
+      // Gate inputs in the Y^T layout: rows 16 kt + r16, channels 16w + 4q4 .. +3.
+      const gchar* zb = uniform_ptr(z + ((b * L + t0) * dm.nheads + h) * kHP + 16 * w);
+      rz[0] = gldr<u32x2>(zb, __umul24((uint32_t)min(r16, last), rowb) + 8 * q4);
+      rz[1] = gldr<u32x2>(zb, __umul24((uint32_t)min(16 + r16, last), rowb) + 8 * q4);
+    }
+  };
+  auto fetch = [&](int64_t c) {
+    const int64_t t0 = c * kQ;
+    const int last = (int)min((int64_t)kQ, L - t0) - 1;
     const gchar* bb = uniform_ptr(B + ((b * L + t0) * dm.ngroups + g) * N);
     const gchar* cb = uniform_ptr(C + ((b * L + t0) * dm.ngroups + g) * N);
 #pragma unroll
@@ -205,14 +221,6 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     if (BT == 256 || w < BT / 64) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) rb[r] = gldr<u32x2>(bb, __umul24((uint32_t)min(4 * tq + r, last), growb) + 8 * bq);
-    }
-    const gchar* db = uniform_ptr(dt + (b * L + t0) * dm.nheads + h);
-    rdt = gldr<uint16_t>(db, __umul24((uint32_t)min(lane, last), (uint32_t)dm.nheads * 2));
-    if (kGate) {
-      // Gate inputs in the Y^T layout: rows 16 kt + r16, channels 16w + 4q4 .. +3.
-      const gchar* zb = uniform_ptr(z + ((b * L + t0) * dm.nheads + h) * kHP + 16 * w);
-      rz[0] = gldr<u32x2>(zb, __umul24((uint32_t)min(r16, last), rowb) + 8 * q4);
-      rz[1] = gldr<u32x2>(zb, __umul24((uint32_t)min(16 + r16, last), rowb) + 8 * q4);
     }
   };
   // x, C and the row copy of B, before the chunk's first barrier.
@@ -249,7 +257,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   };
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
-  if (nchunks > 0) fetch(0);
+  if (nchunks > 0) { fetch(0); fetch_xz(0); }
   for (int64_t c = 0; c < nchunks; ++c) {
     const int buf = (int)(c & 1);
     const int64_t t0 = c * kQ;
@@ -312,6 +320,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     const uint16_t* xp = &sX[(8 * q4 + (r16 >> 2)) * kSX + 16 * w + 4 * (r16 & 3)];
     const u16x8 xt = cat(lds_tr4(xp), lds_tr4(xp + 4 * kSX));
     __syncthreads();  // W complete
+    if (c + 1 < nchunks) fetch_xz(c + 1);
 
     // 4. Y^T = X^T W^T + (H^T C^T) diag(exp(l)); gate; store.
     u16x8 hhi[NK], hlo[NK];
