@@ -14,11 +14,18 @@ int64_t update_grid_blocks(int64_t batch, int64_t d_inner, int32_t d_state);
 
 namespace {
 
-// Target number of resident waves for a full MI355X (256 CUs x 4 SIMDs, two
-// waves per SIMD keep the VALU busy while one waits on memory).
+// Below this many waves an MI355X is underfilled (256 CUs x 4 SIMDs, two waves
+// per SIMD keep the VALU busy while one waits).  At or above it, cutting the
+// sequence into chunks costs more (the summary pass) than it gains (measured
+// on the Mamba-1.4B layer: 2048 waves unchunked 2.1 ms, 2 chunks 2.9 ms).
 constexpr int64_t kTargetWaves = 2048;
+// Once a sequence is cut, aim for this many waves: measured on MI355X, more
+// resident waves pay for the summary pass on the chunks (Mamba-130M layer:
+// 4 chunks 0.27 ms, 32 chunks 0.19 ms; Mamba-2.8B long layer: 4 chunks
+// 4.7 ms, 32 chunks 3.8 ms).
+constexpr int64_t kChunkTargetWaves = 8192;
 // Shortest chunk the automatic plan will cut a sequence into.
-constexpr int64_t kMinAutoChunk = 512;
+constexpr int64_t kMinAutoChunk = 64;
 // Workspace alignment the library asks for.
 constexpr uintptr_t kWorkspaceAlign = 256;
 constexpr uint32_t kKnownFlags = SSM_FLAG_DELTA_SOFTPLUS | SSM_FLAG_EXACT_ZOH;
@@ -60,12 +67,15 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, c
   } else {
     // Each extra wave per tile repeats the per-step fixed work (widening,
     // delta*x, loop and scalar traffic) and adds an LDS exchange: measured
-    // on MI355X, 4 waves per tile cost ~1.4x the VALU work of 1.  So split
-    // the states over at most 2 waves and get further parallelism from
-    // sequence chunks.
-    const int gpref = gmax < 2 ? gmax : (gmin > 2 ? gmin : 2);
+    // on MI355X, 4 waves per tile cost ~1.4x the VALU work of 1, and 2 waves
+    // with chunks lose to 1 wave with more chunks.  So parallelism comes from
+    // sequence chunks; the states are split over a second wave only when the
+    // sequence is too short to cut.
     g = gmin;
-    while (g < gpref && base * g < kTargetWaves) g *= 2;
+    if (seqlen < 2 * kMinAutoChunk) {
+      const int gpref = gmax < 2 ? gmax : (gmin > 2 ? gmin : 2);
+      while (g < gpref && base * g < kTargetWaves) g *= 2;
+    }
   }
   int64_t chunk_len;
   if (o != nullptr && o->chunk_len < 0) return SSM_ERR_UNSUPPORTED;
@@ -75,7 +85,7 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, c
     int64_t nch = 1;
     const int64_t waves = base * g;
     if (waves > 0 && waves < kTargetWaves && seqlen >= 2 * kMinAutoChunk) {
-      nch = (kTargetWaves + waves - 1) / waves;
+      nch = (kChunkTargetWaves + waves - 1) / waves;
       if (nch > seqlen / kMinAutoChunk) nch = seqlen / kMinAutoChunk;
     }
     chunk_len = (seqlen + nch - 1) / nch;

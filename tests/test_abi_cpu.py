@@ -123,12 +123,12 @@ def test_update_argument_errors(lib):
 
 
 @pytest.mark.parametrize("shape,expect_split,expect_chunks", [
-    ((2, 64, 32, 16), 2, 1),            # tiny layer: too short to chunk
-    ((8, 2048, 1536, 16), 2, 4),        # Mamba-130M layer: 2 waves per tile, 4 chunks
+    ((2, 64, 32, 16), 2, 1),            # tiny layer: too short to chunk, so 2 waves per tile
+    ((8, 2048, 1536, 16), 1, 32),       # Mamba-130M layer: 192 tiles, 64-step chunks (the shortest)
     ((32, 4096, 4096, 16), 1, 1),       # Mamba-1.4B layer: enough channels already
-    ((4, 32768, 5120, 16), 2, 4),       # Mamba-2.8B long layer
-    ((1, 65536, 1024, 16), 2, 64),      # one long sequence: many chunks
-    ((2, 4096, 256, 128), 8, 8),        # d_state 128 needs 8 waves per tile
+    ((4, 32768, 5120, 16), 1, 26),      # Mamba-2.8B long layer: ~8192 waves
+    ((1, 65536, 1024, 16), 1, 512),     # one long sequence: many chunks
+    ((2, 4096, 256, 128), 8, 64),       # d_state 128 needs 8 waves per tile
 ])
 def test_launch_plan(lib, shape, expect_split, expect_chunks):
     g, cl, nc = bd.scan_plan(*shape)
