@@ -700,16 +700,21 @@ hipError_t launch_bwd_n(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPla
 
 }  // namespace
 
-// Waves the backward sweep aims for (256 CUs x 4 SIMDs x 2) and the
-// shortest chunk it cuts a sequence into.
-constexpr int64_t kBwdTargetWaves = 2048;
-constexpr int64_t kBwdMinChunk = 256;
+// Below kBwdFillWaves waves from channels (256 CUs x 4 SIMDs x 2) the
+// sequence is cut into chunks, aiming at kBwdChunkTargetWaves waves with
+// chunks of at least kBwdMinChunk steps.  Measured on MI355X: the
+// Mamba-2.8B long layer takes 27.2 ms with ~2048 waves and 17.5 ms with
+// ~16384 (32768: no further gain); the Mamba-1.4B layer (2048 waves) is
+// faster unchunked (11.4 ms against 13.4 ms cut into chunks).
+constexpr int64_t kBwdFillWaves = 2048;
+constexpr int64_t kBwdChunkTargetWaves = 16384;
+constexpr int64_t kBwdMinChunk = 64;
 
 BwdPlan bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner) {
   const int64_t waves = batch * ((d_inner + 63) / 64);
   int64_t nch = 1;
-  if (waves > 0 && waves < kBwdTargetWaves && seqlen >= 2 * kBwdMinChunk) {
-    nch = (kBwdTargetWaves + waves - 1) / waves;
+  if (waves > 0 && waves < kBwdFillWaves && seqlen >= 2 * kBwdMinChunk) {
+    nch = (kBwdChunkTargetWaves + waves - 1) / waves;
     if (nch > seqlen / kBwdMinChunk) nch = seqlen / kBwdMinChunk;
   }
   const int64_t nblk = (seqlen + kBB - 1) / kBB;
