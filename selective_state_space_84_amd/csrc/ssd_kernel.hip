@@ -26,13 +26,19 @@
 //
 // Mapping: one workgroup (4 waves) per (batch row, head) walks the chunks in
 // order; wave w owns channels [16w, 16w+16) of the head, for Y and for H.
-// Per chunk, x, B and C are staged row-major in LDS with 16-byte writes (B
-// and C double-buffered, so two barriers per chunk suffice); the next chunk's
-// rows are loaded into registers while this one computes.
-//   * The operands that run over time (X^T for Y, w o X and B^T for the state
-//     update) need eight consecutive steps per lane: they come from the
-//     row-major tiles through ds_read_b64_tr_b16, which transposes 16 x 4
-//     blocks across each group of 16 lanes.
+// The next chunk's rows are loaded into registers while this one computes
+// and staged in LDS per chunk:
+//   * x row-major; this wave's columns over time (the X^T operand, and w o X)
+//     need eight consecutive steps per lane and come out through
+//     ds_read_b64_tr_b16, which transposes 16 x 4 blocks across each group of
+//     16 lanes.
+//   * B twice: rows in the permuted state order (the score operand), and B^T
+//     for the state update, written transposed (a 4 x 4 transpose in
+//     registers, 4 state rows per padded LDS group) so that every wave reads
+//     it with 16-byte loads.  B^T is written between the chunk's two
+//     barriers, so both copies are single-buffered.
+//   * C in the permuted state order, double-buffered (it is read on both
+//     sides of the second barrier).
 //   * Waves 0-2 each compute one of the three causal 16 x 16 score tiles
 //     (S^T = B C^T), mask them and share W through LDS.
 //   * The state's accumulator layout (lane = channel, four states per lane
@@ -40,7 +46,7 @@
 //     over n takes the states in the order the accumulators hold them, and C
 //     is staged with its columns permuted to match, so the state never
 //     leaves registers.
-//
+
 // MFMA operand layout (checked on the device): for a 16x32 A, lane l holds
 // A[l % 16][8 (l / 16) + j], j < 8; for a 32x16 B, B[8 (l / 16) + j][l % 16];
 // the 16x16 result: D[4 (l / 16) + j][l % 16], j < 4.
