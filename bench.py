@@ -212,13 +212,15 @@ def bench_conv(cfg, steps, dev, d_conv=4):
             "frac_of_8tbs": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "input_gen_s": round(gen_s, 1)}
 
 
-def bench_bwd(cfg, inp, steps, dev):
+def bench_bwd(cfg, inp, steps, dev, flags=0):
     """Gradient of the scan (ssm_scan_bwd) on the scan workload, with
-    seeded upstream gradients dy (io type) and dh_last."""
+    seeded upstream gradients dy (io type) and dh_last, under the same step
+    options (softplus step, exact ZOH) as the forward leg."""
     import torch
     from selective_state_space_84_amd import binding, inputs
     gr = inputs.make_scan_grads(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, 200 + cfg.seed)
-    d = {k: to_dev(inp.get(k), dev) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0")}
+    d = {k: to_dev(inp.get(k), dev) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "dt_bias")}
+    dtb = d["dt_bias"] if flags & binding.SSM_FLAG_DELTA_SOFTPLUS else None
     dy, dhl = to_dev(gr["dy"], dev), to_dev(gr["dh_last"], dev)
     ws = torch.empty(binding.scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state),
                      dtype=torch.uint8, device=dev)
@@ -227,15 +229,15 @@ def bench_bwd(cfg, inp, steps, dev):
     y = torch.empty_like(d["x"])
     hl = torch.empty((cfg.batch, cfg.d_inner, cfg.d_state), dtype=torch.float32, device=dev)
     grads = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], dy=dy,
-                                 dh_last=dhl, workspace=ws)
+                                 dh_last=dhl, workspace=ws, flags=flags, dt_bias=dtb)
 
     def bwd(ckpt=None):
         binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], dy=dy,
-                             dh_last=dhl, workspace=ws, grads=grads, ckpt=ckpt)
+                             dh_last=dhl, workspace=ws, grads=grads, ckpt=ckpt, flags=flags, dt_bias=dtb)
 
     def fwd_ckpt():
         binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], y=y, h_last=hl,
-                             ckpt_out=ck)
+                             ckpt_out=ck, flags=flags, dt_bias=dtb)
 
     def timed(fn):
         for _ in range(2):
@@ -254,13 +256,17 @@ def bench_bwd(cfg, inp, steps, dev):
     ms_fc = timed(fwd_ckpt)
     ms_bc = timed(lambda: bwd(ck))
     el = cfg.batch * cfg.seqlen * cfg.d_inner
-    slots = bwd_slots_per_element(cfg.d_state)
-    frac = el * slots / (ms_bc * 1e-3) / 1e12 / VALU_PEAK_TSLOTS
+    # The slot count is that of the plain step; the options add work it does not count.
+    alu = None
+    if not flags:
+        slots = bwd_slots_per_element(cfg.d_state)
+        frac = el * slots / (ms_bc * 1e-3) / 1e12 / VALU_PEAK_TSLOTS
+        alu = {"min_slots_per_element": slots, "frac_of_valu_peak_bwd_from_ckpt": round(frac, 4)}
     return {"workload": cfg.name + " scan backward (all gradients)", "steps": steps, "ms_per_step": round(ms, 6),
             "elements_per_s": round(el / (ms * 1e-3), 1),
             "training_path": {"fwd_with_ckpt_ms": round(ms_fc, 6), "bwd_from_ckpt_ms": round(ms_bc, 6),
                               "fwd_plus_bwd_ms": round(ms_fc + ms_bc, 6)},
-            "alu": {"min_slots_per_element": slots, "frac_of_valu_peak_bwd_from_ckpt": round(frac, 4)},
+            "alu": alu,
             "workspace_bytes": int(ws.numel()), "ckpt_bytes": int(ck.numel() * 4)}
 
 
@@ -458,8 +464,8 @@ def main():
         out["parity"] = par
     del y, hl
     torch.cuda.empty_cache()
-    if not args.no_bwd and not flags and cfg.d_state <= 16:
-        out["scan_bwd"] = bench_bwd(cfg, inp, max(1, args.steps // 2), dev)
+    if not args.no_bwd and cfg.d_state <= 16:
+        out["scan_bwd"] = bench_bwd(cfg, inp, max(1, args.steps // 2), dev, flags)
         torch.cuda.empty_cache()
     if not args.no_conv:
         out["conv1d"] = bench_conv(cfg, args.steps, dev)

@@ -249,8 +249,10 @@ size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inne
  *   dh0         : [batch][d_inner][d_state] fp32 gradient of the initial state
  *                 (of zeros when h0 is NULL), or NULL.
  *   d_dt_bias   : [d_inner] fp32; required with SSM_FLAG_DELTA_SOFTPLUS.
- *   flags       : 0 or SSM_FLAG_DELTA_SOFTPLUS (SSM_FLAG_EXACT_ZOH returns
- *                 SSM_ERR_UNSUPPORTED).
+ *   flags       : SSM_FLAG_DELTA_SOFTPLUS and/or SSM_FLAG_EXACT_ZOH, as in
+ *                 the forward call.  With the exact ZOH, B's coefficient
+ *                 (exp(delta a) - 1)/a is differentiated in both delta (its
+ *                 derivative is abar) and a.
  *   d_state     : 2, 4, 8 or 16.
  *   workspace   : at least ssm_scan_bwd_workspace_size() bytes, 256-byte
  *                 aligned; contents on entry ignored.

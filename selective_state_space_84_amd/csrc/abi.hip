@@ -302,7 +302,7 @@ int bwd_impl(const void* x, const void* delta, const float* A, const void* B, co
   if (rc != SSM_OK) return rc;
   if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
   if (!bwd_d_state_ok(d_state)) return SSM_ERR_UNSUPPORTED;
-  if (flags & ~(uint32_t)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
+  if (flags & ~kKnownFlags) return SSM_ERR_UNSUPPORTED;
   const bool sp = (flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
   if (!sp) {
     dt_bias = nullptr;

@@ -65,6 +65,24 @@ __device__ __forceinline__ void chunk_blocks(const BwdDims& dm, int c, int& kb, 
 
 __device__ __forceinline__ float sigmoid(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
 
+// d/da of the exact-ZOH coefficient (exp(delta a) - 1)/a, with y = delta *
+// a * log2(e), abar = 2^y, v = y ln 2 and coef from zoh_coef:
+//   |v| >= 1: (delta abar - coef) / a, whose two terms differ by at least a
+//             third of the larger one, so coef's error grows at most ~3x;
+//   |v| < 1:  delta^2 phi'(v), phi'(v) = sum_{k>=0} (k+1) v^k / (k+2)!, to
+//             10 terms (truncation < 1e-7 relative); this also covers a = 0.
+__device__ __forceinline__ float zoh_coef_da(float y, float abar, float delta, float coef, float inv_a) {
+  constexpr float c[10] = {1.f / 2,    2.f / 6,     3.f / 24,     4.f / 120,     5.f / 720,
+                           6.f / 5040, 7.f / 40320, 8.f / 362880, 9.f / 3628800, 10.f / 39916800};
+  const float v = y * kLn2;
+  float p = c[9];
+#pragma unroll
+  for (int k = 8; k >= 0; --k) p = __builtin_fmaf(p, v, c[k]);
+  const float small = delta * delta * p;
+  const float big = __builtin_fmaf(delta, abar, -coef) * inv_a;
+  return __builtin_fabsf(v) < 1.0f ? small : big;
+}
+
 template <typename T>
 __device__ __forceinline__ float gld(const gchar* base, uint32_t off) {
   return io_to_f32(*reinterpret_cast<const T __attribute__((address_space(1)))*>(base + off));
@@ -103,9 +121,11 @@ __global__ void __launch_bounds__(64)
   const float* hs = h_entry != nullptr ? h_entry + (((int64_t)chunk * dm.batch + b) * DI + dc) * N
                                        : (h0 != nullptr ? h0 + (b * DI + dc) * N : nullptr);
   float Al2[N], h[N];
+  float ia[(MODE & kExactZoh) ? N : 1];  // 1/a for the exact-ZOH coefficient
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     Al2[n] = A[dc * N + n] * kLog2e;
+    if (MODE & kExactZoh) ia[n] = 1.0f / A[dc * N + n];
     h[n] = hs != nullptr ? hs[n] : 0.f;
   }
   const float dtb = (MODE & 1) ? dt_bias[dc] : 0.f;
@@ -161,9 +181,18 @@ __global__ void __launch_bounds__(64)
       __builtin_amdgcn_sched_barrier(0);
       float dt = io_to_f32(dr[i]);
       if (MODE & 1) dt = softplus(dt + dtb);
-      const float wx = dt * io_to_f32(xr[i]);
+      const float xv = io_to_f32(xr[i]);
+      const float wx = dt * xv;
 #pragma unroll
-      for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(hw_exp2(dt * Al2[n]), h[n], wx * br.get(n));
+      for (int n = 0; n < N; ++n) {
+        if (MODE & kExactZoh) {
+          const float yv = dt * Al2[n];
+          const float ab = hw_exp2(yv);
+          h[n] = __builtin_fmaf(zoh_coef(yv, ab, dt, ia[n]), xv * br.get(n), ab * h[n]);
+        } else {
+          h[n] = __builtin_fmaf(hw_exp2(dt * Al2[n]), h[n], wx * br.get(n));
+        }
+      }
     }
   }
   if (ke - kb > 1) bq.touch();
@@ -279,8 +308,16 @@ constexpr int bwd_sub() {
   return N * kBB <= 64 ? kBB : 64 / N;
 }
 
+// Waves per SIMD the sweep is compiled for: two, except with the exact ZOH
+// at 16 states, whose extra per-state terms (1/a, the coefficient and its
+// derivative) do not fit 256 VGPRs next to the kept w values.
+template <int N, int MODE>
+constexpr int bwd_sweep_waves() {
+  return ((MODE & kExactZoh) && N >= 16) ? 1 : 2;
+}
+
 template <typename T, int N, int MODE>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_sweep_waves<N, MODE>())))
     k_bwd_sweep(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
                 const T* __restrict__ B, const T* __restrict__ C, const float* __restrict__ D,
                 const T* __restrict__ z, const T* __restrict__ dy, const float* __restrict__ dh_last,
@@ -315,9 +352,11 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
   const float* li = lam_in != nullptr ? lam_in + (((int64_t)chunk * dm.batch + b) * DI + d) * N
                                       : (dh_last != nullptr ? dh_last + (b * DI + d) * N : nullptr);
   float Al2[N], lam[N], gA[N];
+  float ia[(MODE & kExactZoh) ? N : 1];  // 1/a for the exact-ZOH coefficient
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     Al2[n] = A[dc * N + n] * kLog2e;
+    if (MODE & kExactZoh) ia[n] = 1.0f / A[dc * N + n];
     lam[n] = (dvalid && li != nullptr) ? li[n] : 0.f;
     gA[n] = 0.f;
   }
@@ -463,7 +502,15 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
           issue(t0 + i + 1);
           const float dtx = dtp[i] * xv[i];
 #pragma unroll
-          for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(dtx, br.get(n), hw_exp2(dtp[i] * Al2[n]) * h[n]);
+          for (int n = 0; n < N; ++n) {
+            if (MODE & kExactZoh) {
+              const float yv = dtp[i] * Al2[n];
+              const float ab = hw_exp2(yv);
+              h[n] = __builtin_fmaf(zoh_coef(yv, ab, dtp[i], ia[n]), xv[i] * br.get(n), ab * h[n]);
+            } else {
+              h[n] = __builtin_fmaf(dtx, br.get(n), hw_exp2(dtp[i] * Al2[n]) * h[n]);
+            }
+          }
         }
 #pragma unroll
         for (int g0 = 0; g0 < SUB; g0 += GS) {
@@ -479,9 +526,17 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
               float acc = Dv * xv[i];
 #pragma unroll
               for (int n = 0; n < N; ++n) {
-                const float wv = hw_exp2(dtp[i] * Al2[n]) * h[n];
-                w[ii][n] = wv;
-                h[n] = __builtin_fmaf(dtx, br.get(n), wv);
+                if (MODE & kExactZoh) {
+                  const float yv = dtp[i] * Al2[n];
+                  const float ab = hw_exp2(yv);
+                  const float wv = ab * h[n];
+                  w[ii][n] = wv;
+                  h[n] = __builtin_fmaf(zoh_coef(yv, ab, dtp[i], ia[n]), xv[i] * br.get(n), wv);
+                } else {
+                  const float wv = hw_exp2(dtp[i] * Al2[n]) * h[n];
+                  w[ii][n] = wv;
+                  h[n] = __builtin_fmaf(dtx, br.get(n), wv);
+                }
                 acc = __builtin_fmaf(cr.get(n), h[n], acc);
                 red[(s * N + n) * kRedStride + lane] = g[ii] * h[n];
               }
@@ -517,19 +572,35 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             float dti = dt[i];
             asm volatile("" : "+v"(dti));
             const float dtx = dti * xv[i];
-            float dd = 0.f, sb = 0.f;
+            // sb = sum_n lam B (the input term's adjoint per unit coefficient);
+            // with the exact ZOH the coefficient differs per state, so sb
+            // carries it (sum_n lam coef B) and sa = sum_n lam abar B is its
+            // derivative in delta.
+            float dd = 0.f, sb = 0.f, sa = 0.f;
 #pragma unroll
             for (int n = 0; n < N; ++n) {
               lam[n] = __builtin_fmaf(g[ii], cr.get(n), lam[n]);
               const float tw = lam[n] * w[ii][n];
               dd = __builtin_fmaf(tw, Al2[n], dd);
               gA[n] = __builtin_fmaf(dti, tw, gA[n]);
-              sb = __builtin_fmaf(lam[n], br.get(n), sb);
-              red[(s * N + n) * kRedStride + lane] = lam[n] * dtx;
-              lam[n] *= hw_exp2(dti * Al2[n]);
+              if (MODE & kExactZoh) {
+                const float yv = dti * Al2[n];
+                const float ab = hw_exp2(yv);
+                const float coef = zoh_coef(yv, ab, dti, ia[n]);
+                const float lb = lam[n] * br.get(n);
+                sb = __builtin_fmaf(lb, coef, sb);
+                sa = __builtin_fmaf(lb, ab, sa);
+                gA[n] = __builtin_fmaf(lb * xv[i], zoh_coef_da(yv, ab, dti, coef, ia[n]), gA[n]);
+                red[(s * N + n) * kRedStride + lane] = lam[n] * coef * xv[i];
+                lam[n] *= ab;
+              } else {
+                sb = __builtin_fmaf(lam[n], br.get(n), sb);
+                red[(s * N + n) * kRedStride + lane] = lam[n] * dtx;
+                lam[n] *= hw_exp2(dti * Al2[n]);
+              }
             }
-            dxo[ii] = __builtin_fmaf(g[ii], Dv, dti * sb);
-            float ddt = __builtin_fmaf(dd, kLn2, xv[i] * sb);
+            dxo[ii] = (MODE & kExactZoh) ? __builtin_fmaf(g[ii], Dv, sb) : __builtin_fmaf(g[ii], Dv, dti * sb);
+            float ddt = __builtin_fmaf(dd, kLn2, xv[i] * ((MODE & kExactZoh) ? sa : sb));
             if (MODE & 1) ddt *= sg[i];
             accT += ddt;
             ddo[ii] = ddt;
@@ -758,8 +829,13 @@ BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, in
 }
 
 hipError_t launch_scan_bwd(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPlan& pl) {
-  if (p.flags & 1u) return p.bf16 ? launch_bwd_n<uint16_t, 1>(p, ws, pl) : launch_bwd_n<float, 1>(p, ws, pl);
-  return p.bf16 ? launch_bwd_n<uint16_t, 0>(p, ws, pl) : launch_bwd_n<float, 0>(p, ws, pl);
+  // MODE bits as in the forward sweep: kSoftplusDelta, kExactZoh.
+  switch (p.flags & 3u) {
+    case 0: return p.bf16 ? launch_bwd_n<uint16_t, 0>(p, ws, pl) : launch_bwd_n<float, 0>(p, ws, pl);
+    case 1: return p.bf16 ? launch_bwd_n<uint16_t, 1>(p, ws, pl) : launch_bwd_n<float, 1>(p, ws, pl);
+    case 2: return p.bf16 ? launch_bwd_n<uint16_t, 2>(p, ws, pl) : launch_bwd_n<float, 2>(p, ws, pl);
+    default: return p.bf16 ? launch_bwd_n<uint16_t, 3>(p, ws, pl) : launch_bwd_n<float, 3>(p, ws, pl);
+  }
 }
 
 }  // namespace ssm

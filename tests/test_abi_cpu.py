@@ -207,9 +207,14 @@ def test_bwd_argument_errors(lib):
     sp = bd.SSM_FLAG_DELTA_SOFTPLUS
     assert _bwd(lib, flags=sp) == bd.SSM_ERR_NULL_ARG
     assert _bwd(lib, flags=sp, dt_bias=P0 + 8 * MB) == bd.SSM_ERR_NULL_ARG
-    # Unsupported: exact ZOH, unknown flags, d_state outside {2,4,8,16}, dtype.
-    assert _bwd(lib, flags=bd.SSM_FLAG_EXACT_ZOH) == bd.SSM_ERR_UNSUPPORTED
+    # The exact ZOH is accepted (alone and with the softplus step): these calls
+    # get past the flag check and stop at the missing pointer.
+    zoh = bd.SSM_FLAG_EXACT_ZOH
+    assert _bwd(lib, flags=zoh, dx=None) == bd.SSM_ERR_NULL_ARG
+    assert _bwd(lib, flags=zoh | sp, dt_bias=P0 + 8 * MB) == bd.SSM_ERR_NULL_ARG
+    # Unsupported: unknown flags, d_state outside {2,4,8,16}, dtype.
     assert _bwd(lib, flags=0x40) == bd.SSM_ERR_UNSUPPORTED
+    assert _bwd(lib, flags=zoh | 0x40) == bd.SSM_ERR_UNSUPPORTED
     assert _bwd(lib, N=32) == bd.SSM_ERR_UNSUPPORTED
     assert _bwd(lib, N=3) == bd.SSM_ERR_UNSUPPORTED
     assert _bwd(lib, dtype=5) == bd.SSM_ERR_UNSUPPORTED

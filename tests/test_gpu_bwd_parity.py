@@ -14,6 +14,7 @@ from selective_state_space_84_amd import inputs
 pytestmark = pytest.mark.gpu
 
 SP = 0x1  # SSM_FLAG_DELTA_SOFTPLUS
+ZOH = 0x2  # SSM_FLAG_EXACT_ZOH
 
 # Gates on the floored relative error of every gradient.  fp32 io: sized by
 # the float32 emulation in test_tolerance_bwd.py (ddelta's fp32 floor grows
@@ -34,24 +35,26 @@ def _case(batch, L, d, N, dtype, seed, softplus=False, h0=True):
     return inp, gr
 
 
-def _gpu(inp, gr, *, use_D=True, use_z=True, use_h0=True, use_dhl=True, softplus=False, want_dh0=True):
+def _gpu(inp, gr, *, use_D=True, use_z=True, use_h0=True, use_dhl=True, softplus=False, want_dh0=True, zoh=False):
     import torch
     from gpu_util import to_dev, to_host_f64
     from selective_state_space_84_amd import binding
     d = {k: to_dev(inp.get(k)) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "dt_bias")}
     g = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"] if use_D else None,
                              d["z"] if use_z else None, d["h0"] if use_h0 else None, dy=to_dev(gr["dy"]),
-                             dh_last=to_dev(gr["dh_last"]) if use_dhl else None, flags=SP if softplus else 0,
+                             dh_last=to_dev(gr["dh_last"]) if use_dhl else None,
+                             flags=(SP if softplus else 0) | (ZOH if zoh else 0),
                              dt_bias=d["dt_bias"] if softplus else None, want_dh0=want_dh0)
     torch.cuda.synchronize()
     return {k: to_host_f64(v) for k, v in g.items()}
 
 
-def _ref(inp, gr, *, use_D=True, use_z=True, use_h0=True, use_dhl=True, softplus=False):
+def _ref(inp, gr, *, use_D=True, use_z=True, use_h0=True, use_dhl=True, softplus=False, zoh=False):
     return oracle.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"] if use_D else None,
                            inp["z"] if use_z else None, inp["h0"] if use_h0 else None,
                            inp["dt_bias"] if softplus else None, dy=gr["dy"],
-                           dh_last=gr["dh_last"] if use_dhl else None, delta_softplus=softplus)
+                           dh_last=gr["dh_last"] if use_dhl else None, delta_softplus=softplus,
+                           exact_zoh=zoh)
 
 
 def _compare(g, r, gate, keys=None, label=""):
@@ -172,6 +175,48 @@ def test_forward_checkpoints_feed_backward(lib, chunk_len, n_split):
                              dy=to_dev(gr["dy"]), dh_last=to_dev(gr["dh_last"]), ckpt=ck)
     torch.cuda.synchronize()
     _compare({k: to_host_f64(v) for k, v in g.items()}, _ref(inp, gr), F32_GATE, label="ckpt-fed")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("softplus", [False, True])
+@pytest.mark.parametrize("d_state", [4, 16])
+def test_bwd_exact_zoh(lib, dtype, softplus, d_state):
+    """The exact zero-order hold: B's coefficient (exp(delta a) - 1)/a is
+    differentiated in delta and in a (both branches of the coefficient occur:
+    |delta a| spans ~1e-3 to above 1).  Ragged steps and channels."""
+    inp, gr = _case(2, 45, 130, d_state, dtype, 1150 + d_state + 2 * softplus, softplus=softplus)
+    print("case bwd zoh", dtype, softplus, d_state, flush=True)
+    g = _gpu(inp, gr, softplus=softplus, zoh=True)
+    r = _ref(inp, gr, softplus=softplus, zoh=True)
+    _compare(g, r, _gate(dtype), label="zoh %s sp=%d N=%d" % (dtype, softplus, d_state))
+    # The plain-step gradient differs from it at a visible level: the case sees the mode.
+    plain = _ref(inp, gr, softplus=softplus)
+    assert floored_rel_err(plain["dA"], r["dA"]) > 10 * _gate(dtype)
+
+
+@pytest.mark.parametrize("fwd_ckpt", [False, True])
+def test_bwd_exact_zoh_sequence_chunks(lib, fwd_ckpt):
+    """Exact ZOH with the softplus step on a long sequence with few channels
+    (the backward cuts it into chunks; the forward summaries or the forward
+    call's checkpoints use the same coefficient)."""
+    import torch
+    from gpu_util import to_dev, to_host_f64
+    from selective_state_space_84_amd import binding
+    batch, L, dI, N = 2, 1013, 70, 16
+    inp, gr = _case(batch, L, dI, N, "f32", 1760 + fwd_ckpt, softplus=True)
+    print("case zoh chunks", fwd_ckpt, flush=True)
+    d = {k: to_dev(inp.get(k)) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "dt_bias")}
+    ck = None
+    if fwd_ckpt:
+        ck = torch.empty((binding.scan_ckpt_bytes(batch, L, dI, N) // 4,), device="cuda:0")
+        binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], ckpt_out=ck,
+                             flags=SP | ZOH, dt_bias=d["dt_bias"])
+    g = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
+                             dy=to_dev(gr["dy"]), dh_last=to_dev(gr["dh_last"]), flags=SP | ZOH,
+                             dt_bias=d["dt_bias"], ckpt=ck)
+    torch.cuda.synchronize()
+    _compare({k: to_host_f64(v) for k, v in g.items()}, _ref(inp, gr, softplus=True, zoh=True), F32_GATE,
+             label="zoh chunks ckpt=%d" % fwd_ckpt)
 
 
 def _unchunked_ws_bytes(batch, L, d, N):

@@ -50,7 +50,20 @@ def _sigmoid(v, exp2=_exp2):
     return (f(1) / (f(1) + exp2((-v * L2E).astype(np.float32)))).astype(np.float32)
 
 
-def _emulate_bwd(inp, gr, exp2=_exp2):
+def _zoh_terms(dt, A):
+    """The exact-ZOH coefficient (exp(dt a) - 1)/a and its derivative in a,
+    each correctly rounded to fp32 (computed in fp64 from the fp32 operands)."""
+    dt = dt.astype(np.float64)
+    a = A.astype(np.float64)
+    v = dt * a
+    small = np.abs(v) < 1e-8
+    vs = np.where(small, 1.0, v)
+    phi = np.where(small, 1.0 + v / 2, np.expm1(vs) / vs)
+    dphi = np.where(small, 0.5 + v / 3, (vs * np.exp(vs) - np.expm1(vs)) / (vs * vs))
+    return (dt * phi).astype(np.float32), (dt * dt * dphi).astype(np.float32)
+
+
+def _emulate_bwd(inp, gr, exp2=_exp2, exact_zoh=False):
     x, dl, A, Bm, Cm, Dv, z, h0 = (inp[k] for k in ("x", "delta", "A", "B", "C", "D", "z", "h0"))
     dy, dhl = gr["dy"], gr["dh_last"]
     batch, L, d_inner = x.shape
@@ -62,8 +75,12 @@ def _emulate_bwd(inp, gr, exp2=_exp2):
     for t in range(L):
         a = exp2((dl[:, t, :, None] * Al2[None]).astype(np.float32))
         w = (a * h).astype(np.float32)
-        dtx = (dl[:, t] * x[:, t]).astype(np.float32)
-        h = (w + dtx[:, :, None] * Bm[:, t, None, :]).astype(np.float32)
+        if exact_zoh:
+            coef, _ = _zoh_terms(dl[:, t, :, None], A[None])
+            h = (w + coef * (x[:, t, :, None] * Bm[:, t, None, :]).astype(np.float32)).astype(np.float32)
+        else:
+            dtx = (dl[:, t] * x[:, t]).astype(np.float32)
+            h = (w + dtx[:, :, None] * Bm[:, t, None, :]).astype(np.float32)
         ws[t], hs[t] = w, h
     lam = dhl.astype(np.float32).copy()
     dx = np.empty_like(x)
@@ -82,18 +99,36 @@ def _emulate_bwd(inp, gr, exp2=_exp2):
         dz[:, t] = (ypre * (dy[:, t] * s * (f(1) + z[:, t] * (f(1) - s)))).astype(np.float32)
         dC[:, t] = np.einsum("bd,bdn->bn", g.astype(np.float64), hs[t].astype(np.float64)).astype(np.float32)
         dtx = (dl[:, t] * x[:, t]).astype(np.float32)
+        ab = exp2((dl[:, t, :, None] * Al2[None]).astype(np.float32))
+        if exact_zoh:
+            coef, dcda = _zoh_terms(dl[:, t, :, None], A[None])
         dd = np.zeros_like(g)
         sb = np.zeros_like(g)
+        sa = np.zeros_like(g)
         for n in range(N):
             lam[:, :, n] = (lam[:, :, n] + g * Cm[:, t, None, n]).astype(np.float32)
             tw = (lam[:, :, n] * ws[t][:, :, n]).astype(np.float32)
             dd = (dd + tw * Al2[None, :, n]).astype(np.float32)
             dA[:, :, n] = (dA[:, :, n] + dl[:, t] * tw).astype(np.float32)
-            sb = (sb + lam[:, :, n] * Bm[:, t, None, n]).astype(np.float32)
-        dB[:, t] = np.einsum("bdn,bd->bn", lam.astype(np.float64), dtx.astype(np.float64)).astype(np.float32)
-        lam = (lam * exp2((dl[:, t, :, None] * Al2[None]).astype(np.float32))).astype(np.float32)
-        dx[:, t] = (g * Dv[None] + dl[:, t] * sb).astype(np.float32)
-        dd_out[:, t] = (dd * LN2 + x[:, t] * sb).astype(np.float32)
+            if exact_zoh:
+                lb = (lam[:, :, n] * Bm[:, t, None, n]).astype(np.float32)
+                sb = (sb + lb * coef[:, :, n]).astype(np.float32)
+                sa = (sa + lb * ab[:, :, n]).astype(np.float32)
+                dA[:, :, n] = (dA[:, :, n] + (lb * x[:, t]).astype(np.float32) * dcda[:, :, n]).astype(np.float32)
+            else:
+                sb = (sb + lam[:, :, n] * Bm[:, t, None, n]).astype(np.float32)
+        if exact_zoh:
+            lcx = (lam * coef).astype(np.float32) * x[:, t, :, None]
+            dB[:, t] = lcx.astype(np.float64).sum(1).astype(np.float32)
+        else:
+            dB[:, t] = np.einsum("bdn,bd->bn", lam.astype(np.float64), dtx.astype(np.float64)).astype(np.float32)
+        lam = (lam * ab).astype(np.float32)
+        if exact_zoh:
+            dx[:, t] = (g * Dv[None] + sb).astype(np.float32)
+            dd_out[:, t] = (dd * LN2 + x[:, t] * sa).astype(np.float32)
+        else:
+            dx[:, t] = (g * Dv[None] + dl[:, t] * sb).astype(np.float32)
+            dd_out[:, t] = (dd * LN2 + x[:, t] * sb).astype(np.float32)
         dD = (dD + g * x[:, t]).astype(np.float32)
     return {"dx": dx, "ddelta": dd_out, "dz": dz, "dA": dA.sum(0), "dB": dB, "dC": dC, "dD": dD.sum(0),
             "dh0": lam}
@@ -131,3 +166,21 @@ def test_backward_fp32_floor_with_hardware_exp2_model():
         print("trial", trial, " ".join("%s %.2e" % kv for kv in errs.items()))
         worst = max(worst, max(errs.values()))
     assert worst <= BWD_F32_GATE / 3
+
+
+def test_backward_fp32_floor_exact_zoh():
+    """The same gate holds with the exact zero-order hold: its coefficient and
+    the coefficient's derivative in a add one rounding each per state."""
+    global _ULP_RNG
+    inp = inputs.make_scan_inputs(1, 1000, 96, 16, "f32", 1401, nonzero_h0=True)
+    gr = inputs.make_scan_grads(1, 1000, 96, 16, "f32", 1401)
+    ref = oracle.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
+                          dy=gr["dy"], dh_last=gr["dh_last"], exact_zoh=True)
+    _ULP_RNG = np.random.default_rng(7)
+    emu = _emulate_bwd(inp, gr, exp2=_exp2_1ulp, exact_zoh=True)
+    errs = {k: floored_rel_err(emu[k], ref[k]) for k in emu}
+    print(" ".join("%s %.2e" % kv for kv in errs.items()))
+    assert max(errs.values()) <= BWD_F32_GATE / 3
+    # The emulation without the exact ZOH is far off: the check sees the mode.
+    plain = _emulate_bwd(inp, gr)
+    assert floored_rel_err(plain["dA"], ref["dA"]) > 1e-2
