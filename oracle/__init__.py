@@ -53,9 +53,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    # SSM_ORACLE_LIB names a separately built copy of the oracle (the mutation
+    # tests load deliberately broken copies through it); it is never rebuilt.
+    path = os.environ.get("SSM_ORACLE_LIB")
+    if path is None:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     lib.ssm_oracle_scan_f64.argtypes = [P] * 11 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
