@@ -74,6 +74,35 @@ constexpr int row_group() {
   return budget / NS < kTB ? (budget / NS > 0 ? budget / NS : 1) : kTB;
 }
 
+// io rows go through buffer instructions: one resource (4 SGPRs) per tensor
+// over the current block of rows, the lane's byte offset in one VGPR and the
+// row's byte offset in an SGPR shared by all tensors, so an access costs no
+// VALU.  (With plain global pointers the compiler widens the loop-invariant
+// lane offsets to 64 bits outside the loop and adds base and offset per
+// access with a 64-bit VALU add, holding a 64-bit address per row and
+// tensor.)  Raw buffer, byte-addressed: accesses at or past `bytes` read 0 or
+// are dropped.  Word 3 = 0x00020000 sets the gfx9-family data-format field,
+// which raw buffer accesses need to be non-zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+template <typename T>
+__device__ __forceinline__ T buf_ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+template <>
+__device__ __forceinline__ uint16_t buf_ld<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+template <>
+__device__ __forceinline__ float buf_ld<float>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_st(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+}
+
 struct SweepDims {
   int64_t batch, seqlen, d_inner, chunk_len;
   int32_t tiles, n_chunks_grid;  // chunks covered by this launch
@@ -143,25 +172,24 @@ __global__ void __launch_bounds__(64 * (N / NS))
   const float Dv = (!SUMMARY && D != nullptr && wv == 0) ? D[dc] : 0.f;
   const bool has_z = !SUMMARY && z != nullptr;
 
-  // Addressing: x, delta, z and y share one layout, so a block of kTB rows is
-  // reached from one wave-uniform (SGPR) row pointer per tensor plus per-lane
-  // byte offsets voff[i] = (lc + i * d_inner) * sizeof(T), computed once.
-  // Loads and stores then use the SGPR-base form and the per-block pointer
-  // step is the only address arithmetic (scalar) in the steady state.
+  // Addressing: x, delta, z and y share one layout.  Row i of a block is at
+  // byte offset i * row_bytes from the block's first row (xb, db, zb, yb:
+  // wave-uniform), and a lane's element at byte offset lo from there.  The
+  // sizes are bounded (d_inner <= 2^26) so that a block spans at most 2^31
+  // bytes and every offset fits in 32 bits.
   const int64_t row0 = b * dm.seqlen + t_beg;
   const int64_t cbase = (int64_t)tile * 64;
   const int lc = (int)(dc - cbase);
-  uint32_t voff[kTB];
-#pragma unroll
-  for (int i = 0; i < kTB; ++i) voff[i] = (uint32_t)((lc + (int64_t)i * DI) * (int64_t)sizeof(T));
-  const int64_t blk_bytes = (int64_t)kTB * DI * (int64_t)sizeof(T);
+  const uint32_t lo = (uint32_t)lc * (uint32_t)sizeof(T);
+  const uint32_t row_bytes = (uint32_t)(DI * (int64_t)sizeof(T));
+  const uint32_t blk_span = (uint32_t)kTB * row_bytes;
+  const int64_t blk_bytes = blk_span;
   const char* xb = reinterpret_cast<const char*>(x + row0 * DI + cbase);
   const char* db = reinterpret_cast<const char*>(delta + row0 * DI + cbase);
   const char* zb = has_z ? reinterpret_cast<const char*>(z + row0 * DI + cbase) : xb;
   char* yb = SUMMARY ? nullptr : reinterpret_cast<char*>(y + row0 * DI + cbase);
   const T* Bp = B + row0 * N + n0;
   const T* Cp = C + row0 * N + n0;
-  auto ld = [](const char* base, uint32_t off) { return *reinterpret_cast<const T*>(base + off); };
 
   // B/C rows travel in groups of kP steps through SGPRs: the rows of group
   // k+1 are requested as soon as group k's rows have landed, so each request
@@ -185,16 +213,25 @@ __global__ void __launch_bounds__(64 * (N / NS))
   // repeat its last row (only the final blocks of a chunk need it).
   auto fetch = [&](int tb, auto clamp_t) {
     constexpr bool kClamp = decltype(clamp_t)::value;
+    const __amdgpu_buffer_rsrc_t rx = block_rsrc(xb, blk_span), rd = block_rsrc(db, blk_span),
+                                 rz = block_rsrc(zb, blk_span);
 #pragma unroll
     for (int i = 0; i < kTB; ++i) {
-      uint32_t o = voff[i];
-      if (kClamp) {
-        const int ii = min(tb + i, nsteps - 1) - tb;
-        o = (uint32_t)((lc + (int64_t)ii * DI) * (int64_t)sizeof(T));
-      }
-      xn[i] = ld(xb, o);
-      dn[i] = ld(db, o);
-      if (has_z && own(i)) zn[i] = ld(zb, o);
+      const int ii = kClamp ? min(tb + i, nsteps - 1) - tb : i;
+      const uint32_t so = (uint32_t)ii * row_bytes;
+      xn[i] = buf_ld<T>(rx, lo, so);
+      dn[i] = buf_ld<T>(rd, lo, so);
+      // Not under the runtime has_z (zb is x's rows when there is no gate): a
+      // load under a runtime condition keeps zn in scratch memory.
+      if (!SUMMARY && own(i)) zn[i] = buf_ld<T>(rz, lo, so);
+    }
+  };
+  auto store_y = [&](int i, float v) {
+    // Narrowed in registers (RNE for bf16) and stored through the block's resource.
+    if constexpr (sizeof(T) == 2) {
+      buf_st(__builtin_bit_cast(uint16_t, (__bf16)v), block_rsrc(yb, blk_span), lo, (uint32_t)i * row_bytes);
+    } else {
+      buf_st(v, block_rsrc(yb, blk_span), lo, (uint32_t)i * row_bytes);
     }
   };
   fetch(0, std::integral_constant<bool, true>{});
@@ -211,18 +248,22 @@ __global__ void __launch_bounds__(64 * (N / NS))
   // (callers guarantee tb + 2 * kTB <= nsteps).
   // Checkpoints for the backward pass: the state before every block of kTB
   // steps (chunks start on block boundaries when this is requested).
-  float* ck = (!SUMMARY && dm.ckpt != nullptr)
-                  ? dm.ckpt + ((b * ((dm.seqlen + kTB - 1) / kTB) + t_beg / kTB) * N + n0) * DI + d
-                  : nullptr;
-  const int64_t ck_step = (int64_t)N * DI;  // floats between consecutive blocks
+  char* ck = (!SUMMARY && dm.ckpt != nullptr)
+                 ? reinterpret_cast<char*>(dm.ckpt +
+                                           ((b * ((dm.seqlen + kTB - 1) / kTB) + t_beg / kTB) * N + n0) * DI + cbase)
+                 : nullptr;
+  const uint32_t ck_row = (uint32_t)(DI * (int64_t)sizeof(float));  // bytes between states (<= 2^28)
+  const int64_t ck_step = (int64_t)N * ck_row;                        // bytes between consecutive blocks
 
   auto block = [&](int tb, auto full_t) {
     constexpr bool kFull = decltype(full_t)::value;
     const int nt = kFull ? kTB : min(kTB, nsteps - tb);
     if (!SUMMARY && ck != nullptr) {
       if (dvalid) {
+        // The last state row starts below 2^32 - 2^28; no bound is needed.
+        const __amdgpu_buffer_rsrc_t rc = block_rsrc(ck, 0xffffffffu);
 #pragma unroll
-        for (int n = 0; n < NS; ++n) ck[(int64_t)n * DI] = h[n];
+        for (int n = 0; n < NS; ++n) buf_st(h[n], rc, (uint32_t)lc * 4u, (uint32_t)n * ck_row);
       }
       ck += ck_step;
     }
@@ -316,7 +357,7 @@ __global__ void __launch_bounds__(64 * (N / NS))
         if (dvalid) {
 #pragma unroll
           for (int i = 0; i < kTB; ++i)
-            if (kFull || i < nt) io_store(reinterpret_cast<T*>(yb + voff[i]), part[i]);
+            if (kFull || i < nt) store_y(i, part[i]);
         }
       } else {
         float* mine = red + ((buf * G + wv) * kTB) * 64 + lane;
@@ -331,7 +372,7 @@ __global__ void __launch_bounds__(64 * (N / NS))
 #pragma unroll
             for (int j = 0; j < G; ++j) v += base[(j * kTB + i) * 64];
             if (has_z) v *= silu(io_to_f32(zr[i]));
-            if (dvalid) io_store(reinterpret_cast<T*>(yb + voff[i]), v);
+            if (dvalid) store_y(i, v);
           }
         }
         buf ^= 1;
