@@ -17,13 +17,14 @@ namespace {
 // Below this many waves an MI355X is underfilled (256 CUs x 4 SIMDs, two waves
 // per SIMD keep the VALU busy while one waits).  At or above it, cutting the
 // sequence into chunks costs more (the summary pass) than it gains (measured
-// on the Mamba-1.4B layer: 2048 waves unchunked 2.1 ms, 2 chunks 2.9 ms).
+// on the Mamba-1.4B layer: 2048 waves unchunked 1.99 ms, 2 chunks 2.34 ms,
+// 4 chunks 2.41 ms; 2 waves per tile 2.04 ms).
 constexpr int64_t kTargetWaves = 2048;
 // Once a sequence is cut, aim for this many waves: measured on MI355X, more
-// resident waves pay for the summary pass on the chunks (Mamba-130M layer:
-// 4 chunks 0.27 ms, 32 chunks 0.19 ms; Mamba-2.8B long layer: 4 chunks
-// 4.7 ms, 32 chunks 3.8 ms).
-constexpr int64_t kChunkTargetWaves = 8192;
+// resident waves pay for the summary pass on the chunks (Mamba-2.8B long
+// layer, 320 waves from channels: 8 chunks 4.31 ms, 26 chunks 3.73 ms, 32 or
+// 64 chunks 3.26 ms; Mamba-130M layer: 8 chunks 0.21 ms, 32 chunks 0.17 ms).
+constexpr int64_t kChunkTargetWaves = 16384;
 // Shortest chunk the automatic plan will cut a sequence into.
 constexpr int64_t kMinAutoChunk = 64;
 // Workspace alignment the library asks for.

@@ -126,8 +126,8 @@ def test_update_argument_errors(lib):
     ((2, 64, 32, 16), 2, 1),            # tiny layer: too short to chunk, so 2 waves per tile
     ((8, 2048, 1536, 16), 1, 32),       # Mamba-130M layer: 192 tiles, 64-step chunks (the shortest)
     ((32, 4096, 4096, 16), 1, 1),       # Mamba-1.4B layer: enough channels already
-    ((4, 32768, 5120, 16), 1, 26),      # Mamba-2.8B long layer: ~8192 waves
-    ((1, 65536, 1024, 16), 1, 512),     # one long sequence: many chunks
+    ((4, 32768, 5120, 16), 1, 52),      # Mamba-2.8B long layer: ~16384 waves
+    ((1, 65536, 1024, 16), 1, 1024),    # one long sequence: 64-step chunks (the shortest)
     ((2, 4096, 256, 128), 8, 64),       # d_state 128 needs 8 waves per tile
 ])
 def test_launch_plan(lib, shape, expect_split, expect_chunks):
