@@ -179,3 +179,108 @@ def test_full_size_config_sampled(lib, name):
     eh = floored_rel_err(hs, rh)
     print(name, "sampled errors y %.3g h %.3g" % (ey, eh), flush=True)
     assert ey <= 2e-2 and eh <= 2e-2
+
+
+# The largest d_inner the library accepts (2^26).  With fp32 io a row of one
+# timestep is 2^28 bytes and an 8-step block 2^31 bytes: the largest offsets
+# the sweep's 32-bit (buffer) addressing has to carry.  Checkpoints at
+# d_state 16 reach state row 15 at 15 * 2^28 bytes.
+_MAX_DI = 1 << 26
+
+
+def _max_di_inputs(L, N, seed):
+    """Seeded inputs generated on the device (the host copies would be tens of
+    GB): x, z, B, C ~ N(0, 1), steps ~ U[0.001, 0.1], A = -(n+1), D = 1,
+    h0 ~ N(0, 0.1^2), fp32."""
+    import torch
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(seed)
+    dev = "cuda:0"
+    d = {"x": torch.randn((1, L, _MAX_DI), generator=g, device=dev),
+         "delta": torch.rand((1, L, _MAX_DI), generator=g, device=dev) * 0.099 + 0.001,
+         "z": torch.randn((1, L, _MAX_DI), generator=g, device=dev),
+         "B": torch.randn((1, L, N), generator=g, device=dev),
+         "C": torch.randn((1, L, N), generator=g, device=dev),
+         "A": -torch.arange(1, N + 1, dtype=torch.float32, device=dev).repeat(_MAX_DI, 1),
+         "D": torch.ones(_MAX_DI, device=dev),
+         "h0": 0.1 * torch.randn((1, _MAX_DI, N), generator=g, device=dev)}
+    return d
+
+
+def _max_di_channels(seed, k=24):
+    rng = np.random.default_rng(seed)
+    picks = {0, 1, 63, 64, (1 << 25) + 7, _MAX_DI - 65, _MAX_DI - 64, _MAX_DI - 1}
+    while len(picks) < k:
+        picks.add(int(rng.integers(_MAX_DI)))
+    return sorted(picks)
+
+
+def _oracle_on_channels(d, chans, steps=None):
+    """The oracle on the chosen channels only (each channel is independent)."""
+    import torch
+    ci = torch.tensor(chans, device="cuda:0")
+    L = d["x"].shape[1] if steps is None else steps
+    cut = lambda t: t[:, :L].index_select(2, ci).double().cpu().numpy()
+    return oracle.scan(cut(d["x"]), cut(d["delta"]), d["A"].index_select(0, ci).double().cpu().numpy(),
+                       d["B"][:, :L].double().cpu().numpy(), d["C"][:, :L].double().cpu().numpy(),
+                       d["D"].index_select(0, ci).double().cpu().numpy(), cut(d["z"]),
+                       d["h0"].index_select(1, ci).double().cpu().numpy())
+
+
+@pytest.mark.parametrize("chunk_len", [0, 8])
+def test_max_d_inner_fp32(lib, chunk_len):
+    """d_inner = 2^26 with fp32 io, 17 steps (a full block, a partial one and a
+    one-step tail), unchunked and in 8-step chunks (summary sweep, carry)."""
+    import torch
+    from selective_state_space_84_amd import binding
+    L, N = 17, 2
+    # Host-side bound check of the offsets this launch uses (row, block, lane).
+    row_bytes = _MAX_DI * 4
+    assert 8 * row_bytes <= 1 << 31 and 7 * row_bytes + 63 * 4 < 1 << 31
+    print("case max d_inner fp32 chunk_len", chunk_len, flush=True)
+    d = _max_di_inputs(L, N, 4242 + chunk_len)
+    y, hl = binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
+                                 chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    chans = _max_di_channels(77 + chunk_len)
+    ci = torch.tensor(chans, device="cuda:0")
+    gy = y.index_select(2, ci).double().cpu().numpy()
+    gh = hl.index_select(1, ci).double().cpu().numpy()
+    ry, rh = _oracle_on_channels(d, chans)
+    del y, hl, d
+    torch.cuda.empty_cache()
+    ey, eh = floored_rel_err(gy, ry), floored_rel_err(gh, rh)
+    print("max d_inner errors y %.3g h %.3g" % (ey, eh), flush=True)
+    assert ey <= 1e-5 and eh <= 1e-5
+
+
+def test_max_d_inner_checkpoints(lib):
+    """d_inner = 2^26, d_state 16, checkpoint output: every block-start state of
+    the sampled channels (state rows up to 15 * 2^28 bytes into a block's
+    checkpoint rows) equals the oracle's state after 0, 8 and 16 steps."""
+    import torch
+    from selective_state_space_84_amd import binding
+    L, N = 17, 16
+    assert 15 * _MAX_DI * 4 + 63 * 4 + 4 <= (1 << 32) - 1
+    print("case max d_inner checkpoints", flush=True)
+    d = _max_di_inputs(L, N, 4300)
+    nblk = -(-L // 8)
+    ck = torch.empty((binding.scan_ckpt_bytes(1, L, _MAX_DI, N) // 4,), device="cuda:0")
+    y, hl = binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], ckpt_out=ck)
+    torch.cuda.synchronize()
+    chans = _max_di_channels(78, k=12)
+    ci = torch.tensor(chans, device="cuda:0")
+    gck = ck.view(nblk, N, _MAX_DI).index_select(2, ci).double().cpu().numpy()
+    gy = y.index_select(2, ci).double().cpu().numpy()
+    del y, hl, ck
+    ry, _ = _oracle_on_channels(d, chans)
+    ref = [d["h0"].index_select(1, ci).double().cpu().numpy()[0]]
+    for k in range(1, nblk):
+        ref.append(_oracle_on_channels(d, chans, steps=8 * k)[1][0])
+    del d
+    torch.cuda.empty_cache()
+    assert floored_rel_err(gy, ry) <= 1e-5
+    for k in range(nblk):
+        e = floored_rel_err(gck[k].T, ref[k])
+        print("checkpoint", k, "error %.3g" % e, flush=True)
+        assert e <= 1e-5, k
