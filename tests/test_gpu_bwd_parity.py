@@ -333,3 +333,45 @@ def test_bwd_full_size_mamba_1p4b(lib):
         rA[chans.index(dd)] += a
         rD[chans.index(dd)] += dv
     _compare({"dA": dA, "dD": dD}, {"dA": rA, "dD": rD}, F32_GATE, label="1.4b dA/dD")
+
+
+def test_bwd_max_d_inner(lib):
+    """d_inner = 2^26 (the largest accepted) with fp32 io, 17 steps: the
+    backward's 32-bit row offsets reach 7 * 2^28 bytes.  Inputs and upstream
+    gradients are generated on the device; the per-channel gradients (dx,
+    ddelta, dz, dA, dD, dh0) of sampled channels are compared with the oracle
+    run on those channels (dB and dC sum over every channel and are covered
+    by the smaller cases)."""
+    import torch
+    from selective_state_space_84_amd import binding
+    DI, L, N = 1 << 26, 17, 2
+    assert 7 * DI * 4 + 63 * 4 < 1 << 31
+    print("case bwd max d_inner", flush=True)
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(4400)
+    dev = "cuda:0"
+    d = {"x": torch.randn((1, L, DI), generator=g, device=dev),
+         "delta": torch.rand((1, L, DI), generator=g, device=dev) * 0.099 + 0.001,
+         "z": torch.randn((1, L, DI), generator=g, device=dev),
+         "B": torch.randn((1, L, N), generator=g, device=dev),
+         "C": torch.randn((1, L, N), generator=g, device=dev),
+         "A": -torch.arange(1, N + 1, dtype=torch.float32, device=dev).repeat(DI, 1),
+         "D": torch.ones(DI, device=dev),
+         "h0": 0.1 * torch.randn((1, DI, N), generator=g, device=dev),
+         "dy": torch.randn((1, L, DI), generator=g, device=dev),
+         "dh_last": torch.randn((1, DI, N), generator=g, device=dev)}
+    gr = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], dy=d["dy"],
+                              dh_last=d["dh_last"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4401)
+    chans = sorted({0, 1, 63, 64, (1 << 25) + 7, DI - 65, DI - 64, DI - 1} | {int(v) for v in rng.integers(DI, size=8)})
+    ci = torch.tensor(chans, device=dev)
+    host = lambda t, dim: t.index_select(dim, ci).double().cpu().numpy()
+    got = {"dx": host(gr["dx"], 2), "ddelta": host(gr["ddelta"], 2), "dz": host(gr["dz"], 2),
+           "dA": host(gr["dA"], 0), "dD": host(gr["dD"], 0), "dh0": host(gr["dh0"], 1)}
+    ref = oracle.scan_bwd(host(d["x"], 2), host(d["delta"], 2), host(d["A"], 0), d["B"].double().cpu().numpy(),
+                          d["C"].double().cpu().numpy(), host(d["D"], 0), host(d["z"], 2), host(d["h0"], 1),
+                          dy=host(d["dy"], 2), dh_last=host(d["dh_last"], 1))
+    del gr, d
+    torch.cuda.empty_cache()
+    _compare(got, ref, F32_GATE, keys=list(got), label="bwd max d_inner")
