@@ -145,9 +145,18 @@ def bench_scan(cfg, steps, warmup, dev, n_split=0, chunk_len=0, flags=0):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # Spread: the same steps again, each between its own pair of events.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    spread = {"median": round(per[len(per) // 2], 6), "min": round(per[0], 6), "max": round(per[-1], 6)}
     step(0)  # y, hl of the first set (every set holds the same inputs)
     torch.cuda.synchronize()
-    return inp, y, hl, ms, gen_s, (g, chunk_len, n_chunks, len(sets))
+    return inp, y, hl, ms, gen_s, (g, chunk_len, n_chunks, len(sets)), spread
 
 
 def bench_decode(steps, dev):
@@ -395,11 +404,19 @@ def cpu_baseline(cfg, inp, y_dev, hl_dev, cpu_budget_s=24.0, flags=0):
                 g = yb.cpu().numpy().astype(np.float64)
             worst_y = max(worst_y, err(g, ry))
             worst_h = max(worst_h, err(hl_dev[b].cpu().numpy().astype(np.float64), rh))
+    # The same oracle on one thread: one slice of row 0.
+    t0 = time.perf_counter()
+    run_slice(0, 0)
+    t1 = time.perf_counter() - t0
+    el1 = cfg.seqlen * min(width, cfg.d_inner)
     return {
         "value": round(el / spent, 1), "unit": "elements/s", "cores": threads, "kind": "oracle",
         "sample": "batch rows 0..%d of the same workload (all %d channels x %d timesteps each, %d elements), "
                   "fp64 C loop on %d threads over %d-channel slices, %.2f s wall" % (
                       rows - 1, cfg.d_inner, cfg.seqlen, el, threads, width, spent),
+        "single_thread": {"value": round(el1 / t1, 1), "unit": "elements/s", "cores": 1,
+                          "sample": "channels 0..%d of row 0 (%d elements), %.3f s" % (
+                              min(width, cfg.d_inner) - 1, el1, t1)},
     }, {"rows_checked": rows, "y_err": worst_y, "h_last_err": worst_h,
         "metric": "max |g-r| / max(|r|, 0.1 rms(r)) vs fp64 oracle", "gate": 2e-2 if cfg.dtype == "bf16" else 1e-5}
 
@@ -438,7 +455,7 @@ def main():
     if unknown:
         ap.error("unknown --flags %s (known: %s)" % (",".join(unknown), ",".join(flag_bits)))
     flags = sum(flag_bits[f] for f in flag_names)
-    inp, y, hl, ms, gen_s, (g, chunk_len, n_chunks, n_sets) = bench_scan(cfg, args.steps, args.warmup, dev,
+    inp, y, hl, ms, gen_s, (g, chunk_len, n_chunks, n_sets), spread = bench_scan(cfg, args.steps, args.warmup, dev,
                                                                        args.n_split, args.chunk_len, flags)
     el = cfg.batch * cfg.seqlen * cfg.d_inner
     io_bytes = 2 if cfg.dtype == "bf16" else 4
@@ -457,6 +474,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
+        "step_ms": spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
