@@ -21,9 +21,10 @@
 // only what the backward pass needs).
 //
 // Mapping onto CDNA4 (lane = channel, as in the forward sweep):
-//   1. k_bwd_ckpt: a forward sweep that stores the state at the start of every
-//      block of kBB = 8 steps: ckpt[b][k][n][d], so each state row is one
-//      coalesced 256-byte line per wave.
+//   1. Checkpoints: the state at the start of every block of kBB = 8 steps,
+//      ckpt[b][k][n][d] (each state row one coalesced line per wave), from
+//      the forward scan's checkpoint output or, in a standalone call, from
+//      the forward sweep's state-only mode (k_scan_sweep, summary mode).
 //   2. k_bwd_sweep: one wave per (batch row, 64-channel tile) walks the blocks
 //      from last to first.  A block is recomputed forward from its checkpoint,
 //      keeping abar * h_{t-1} for its steps in VGPRs (the recurrence's inputs
@@ -92,110 +93,6 @@ __device__ __forceinline__ void gst(gchar* base, uint32_t off, float v) {
   T bits;
   io_store(&bits, v);
   *reinterpret_cast<T __attribute__((address_space(1)))*>(base + off) = bits;
-}
-
-// ckpt[b][k][n][d] = state before step k * kBB, k = 0 .. nblk-1 (used when
-// the forward call did not save them).  B rows arrive one step ahead
-// through SGPRs; x and delta one block ahead.
-template <typename T, int N, int MODE>
-__global__ void __launch_bounds__(64)
-    k_bwd_ckpt(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
-               const T* __restrict__ B, const float* __restrict__ h0, const float* __restrict__ dt_bias,
-               float* __restrict__ ckpt, const float* __restrict__ h_entry, const BwdDims dm) {
-  const int lane = threadIdx.x;
-  int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = bid % dm.tiles;
-  bid /= dm.tiles;
-  const int chunk = bid % dm.n_chunks;
-  const int64_t b = bid / dm.n_chunks;
-  const int64_t DI = dm.d_inner, L = dm.seqlen;
-  const int64_t d = (int64_t)tile * 64 + lane;
-  const bool dvalid = d < DI;
-  const int64_t dc = dvalid ? d : DI - 1;
-  const int64_t cbase = (int64_t)tile * 64;
-  const int lc = (int)(dc - cbase);
-  int kb, ke;
-  chunk_blocks(dm, chunk, kb, ke);
-
-  // Start state: h0 for one chunk, else the chunk's entry state.
-  const float* hs = h_entry != nullptr ? h_entry + (((int64_t)chunk * dm.batch + b) * DI + dc) * N
-                                       : (h0 != nullptr ? h0 + (b * DI + dc) * N : nullptr);
-  float Al2[N], h[N];
-  float ia[(MODE & kExactZoh) ? N : 1];  // 1/a for the exact-ZOH coefficient
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    Al2[n] = A[dc * N + n] * kLog2e;
-    if (MODE & kExactZoh) ia[n] = 1.0f / A[dc * N + n];
-    h[n] = hs != nullptr ? hs[n] : 0.f;
-  }
-  const float dtb = (MODE & 1) ? dt_bias[dc] : 0.f;
-  const uint32_t row_bytes = (uint32_t)(DI * (int64_t)sizeof(T));
-  uint32_t voff[kBB];
-#pragma unroll
-  for (int i = 0; i < kBB; ++i) voff[i] = (uint32_t)lc * (uint32_t)sizeof(T) + (uint32_t)i * row_bytes;
-  auto rowp = [&](const void* base, int64_t t) {
-    return uniform_ptr(reinterpret_cast<const char*>(base) + ((b * L + t) * DI + cbase) * (int64_t)sizeof(T));
-  };
-  const T* Bb = B + b * L * N;
-  float* cp = ckpt + b * dm.nblk * N * DI + d;
-
-  // Only blocks kb .. ke-2 are stepped through (the state after the chunk's
-  // last block is not needed), and all of them are full.
-  // Raw values: widening happens at use, so the next block's loads stay in
-  // flight while this block computes.
-  T xn[kBB], dn[kBB];
-  auto fetch = [&](int k) {
-    const gchar* xb = rowp(x, (int64_t)k * kBB);
-    const gchar* db = rowp(delta, (int64_t)k * kBB);
-#pragma unroll
-    for (int i = 0; i < kBB; ++i) {
-      xn[i] = gldr<T>(xb, voff[i]);
-      dn[i] = gldr<T>(db, voff[i]);
-    }
-  };
-  StateRow<T, N> bq;
-  if (ke - kb > 1) {
-    fetch(kb);
-    bq.load(Bb + (int64_t)kb * kBB * N);
-  }
-  for (int k = kb; k < ke; ++k) {
-    if (dvalid) {
-#pragma unroll
-      for (int n = 0; n < N; ++n) cp[((int64_t)k * N + n) * DI] = h[n];
-    }
-    if (k + 1 >= ke) break;
-    T xr[kBB], dr[kBB];
-#pragma unroll
-    for (int i = 0; i < kBB; ++i) {
-      xr[i] = xn[i];
-      dr[i] = dn[i];
-    }
-    if (k + 2 < ke) fetch(k + 1);
-#pragma unroll
-    for (int i = 0; i < kBB; ++i) {
-      bq.touch();
-      __builtin_amdgcn_sched_barrier(0);
-      const StateRow<T, N> br = bq;
-      // The next row is at most (ke - 1) * kBB < seqlen.
-      bq.load(Bb + ((int64_t)k * kBB + i + 1) * N);
-      __builtin_amdgcn_sched_barrier(0);
-      float dt = io_to_f32(dr[i]);
-      if (MODE & 1) dt = softplus(dt + dtb);
-      const float xv = io_to_f32(xr[i]);
-      const float wx = dt * xv;
-#pragma unroll
-      for (int n = 0; n < N; ++n) {
-        if (MODE & kExactZoh) {
-          const float yv = dt * Al2[n];
-          const float ab = hw_exp2(yv);
-          h[n] = __builtin_fmaf(zoh_coef(yv, ab, dt, ia[n]), xv * br.get(n), ab * h[n]);
-        } else {
-          h[n] = __builtin_fmaf(hw_exp2(dt * Al2[n]), h[n], wx * br.get(n));
-        }
-      }
-    }
-  }
-  if (ke - kb > 1) bq.touch();
 }
 
 // Adjoint summary of chunk c >= 1: processing its steps backwards maps the
@@ -721,8 +618,13 @@ hipError_t launch_bwd_t(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPla
         if (e != hipSuccess) return e;
         h_entry = ws.fH;
       }
-      e = launch(k_bwd_ckpt<T, N, MODE>, dim3(waves * nch), dim3(64), 0, p.stream, x, dl, p.A, Bm, p.h0,
-                 p.dt_bias, ws.ckpt, h_entry, dm);
+      // The checkpoints: the forward sweep's state-only (summary) mode, run
+      // from each chunk's entry state, writes the state before every block.
+      SweepDims cd{p.batch, p.seqlen, p.d_inner, pl.chunk_len, (int32_t)tiles, nch, nch, h_entry != nullptr ? 1 : 0,
+                   ws.ckpt};
+      e = launch(k_scan_sweep<T, N, N, true, MODE>, dim3(waves * nch), dim3(64), 0, p.stream, x, dl, p.A, Bm, Cm,
+                 (const float*)nullptr, zz, h_entry != nullptr ? h_entry : p.h0, (T*)nullptr, (float*)nullptr,
+                 (float*)nullptr, (float*)nullptr, p.dt_bias, cd);
       if (e != hipSuccess) return e;
       ck = ws.ckpt;
     }

@@ -113,8 +113,11 @@ struct SweepDims {
 
 // One sweep over a (batch row, chunk, 64-channel tile).  N = d_state, NS =
 // states per wave, G = N / NS waves per workgroup.
-// SUMMARY = true: chunk summary (state from zero, no readout): writes
-// P = exp(A * sum(delta)) and the end state S of chunk c into sumP / sumS.
+// SUMMARY = true: no readout.  As the chunk summary (h_init and sumP null:
+// state from zero) it writes P = exp(A * sum(delta)) and the end state S of
+// chunk c into sumP / sumS; given h_init and checkpoints instead (and null
+// sumP / sumS) it is the state-only sweep that writes the checkpoints for
+// the backward pass.
 // SUMMARY = false: full sweep with readout, gate, y store and h_last.
 template <typename T, int N, int NS, bool SUMMARY, int MODE>
 __global__ void __launch_bounds__(64 * (N / NS))
@@ -160,7 +163,7 @@ __global__ void __launch_bounds__(64 * (N / NS))
     }
   }
   const float dtb = (MODE & kSoftplusDelta) ? dt_bias[dc] : 0.f;
-  if (!SUMMARY && h_init != nullptr) {
+  if (h_init != nullptr) {
     const int64_t row = dm.h_init_chunked ? ((int64_t)chunk * dm.batch + b) * DI + dc : b * DI + dc;
     const float* hp = h_init + row * N + n0;
 #pragma unroll
@@ -248,7 +251,7 @@ __global__ void __launch_bounds__(64 * (N / NS))
   // (callers guarantee tb + 2 * kTB <= nsteps).
   // Checkpoints for the backward pass: the state before every block of kTB
   // steps (chunks start on block boundaries when this is requested).
-  char* ck = (!SUMMARY && dm.ckpt != nullptr)
+  char* ck = dm.ckpt != nullptr
                  ? reinterpret_cast<char*>(dm.ckpt +
                                            ((b * ((dm.seqlen + kTB - 1) / kTB) + t_beg / kTB) * N + n0) * DI + cbase)
                  : nullptr;
@@ -258,7 +261,7 @@ __global__ void __launch_bounds__(64 * (N / NS))
   auto block = [&](int tb, auto full_t) {
     constexpr bool kFull = decltype(full_t)::value;
     const int nt = kFull ? kTB : min(kTB, nsteps - tb);
-    if (!SUMMARY && ck != nullptr) {
+    if (ck != nullptr) {
       if (dvalid) {
         // The last state row starts below 2^32 - 2^28; no bound is needed.
         const __amdgpu_buffer_rsrc_t rc = block_rsrc(ck, 0xffffffffu);
@@ -391,7 +394,7 @@ __global__ void __launch_bounds__(64 * (N / NS))
   asm volatile("" ::"v"(pf_sink ^ pf_last));
 
   if (SUMMARY) {
-    if (dvalid) {
+    if (sumP != nullptr && dvalid) {
       const int64_t o = (((int64_t)chunk * dm.batch + b) * DI + d) * N + n0;
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
@@ -426,6 +429,7 @@ hipError_t launch_scan_t(const ScanLaunch& p) {
     float* hent = sumS + (p.n_chunks - 1) * states;
     SweepDims ds = dm;
     ds.n_chunks_grid = (int32_t)(p.n_chunks - 1);
+    ds.ckpt = nullptr;  // the summaries start from zero: only the main sweep writes checkpoints
     e = launch(k_scan_sweep<T, N, NS, true, MODE>, dim3((unsigned)(p.batch * (p.n_chunks - 1) * tiles)), dim3(64 * G), 0,
                p.stream, x, dl, p.A, Bm, Cm, p.D, zz, (const float*)nullptr, y, p.h_last, sumP, sumS, p.dt_bias, ds);
     if (e != hipSuccess) return e;
