@@ -541,6 +541,26 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
   }
 }
 
+// sum over k = 0..count-1 of p[k * stride], in a fixed order: eight partial
+// sums (k mod 8) added pairwise at the end, so that eight loads are in flight
+// per thread (one running sum waits for every load in turn: with few
+// elements per launch, such as the Mamba-130M layer's 24576 dA entries over
+// 256 rows, that latency chain was the whole cost).
+__device__ __forceinline__ float strided_sum(const float* __restrict__ p, int64_t count, int64_t stride) {
+  float s[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s[j] = 0.f;
+  int64_t k = 0;
+  for (; k + 8 <= count; k += 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] += p[(k + j) * stride];
+  }
+#pragma unroll
+  for (int j = 0; j < 7; ++j)
+    if (k + j < count) s[j] += p[(k + j) * stride];
+  return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+}
+
 // dB[r][n] = sum over tiles of part[tile][r][n], dC[r][n] likewise from
 // column N + n; r runs over (b, t).
 __global__ void __launch_bounds__(256) k_bwd_reduce_bc(const float* __restrict__ part, float* __restrict__ dB,
@@ -549,8 +569,7 @@ __global__ void __launch_bounds__(256) k_bwd_reduce_bc(const float* __restrict__
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = rows * 2 * N;
   if (i >= total) return;
-  float s = 0.f;
-  for (int t = 0; t < tiles; ++t) s += part[(int64_t)t * total + i];
+  const float s = strided_sum(part + i, tiles, total);
   const int64_t r = i / (2 * N);
   const int c = (int)(i - r * 2 * N);
   if (c < N) {
@@ -568,22 +587,10 @@ __global__ void __launch_bounds__(256) k_bwd_reduce_params(const float* __restri
                                                            int64_t batch, int64_t d_inner, int32_t N) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t na = d_inner * N;
-  if (i < na) {
-    float s = 0.f;
-    for (int64_t b = 0; b < batch; ++b) s += part_a[b * na + i];
-    dA[i] = s;
-  }
+  if (i < na) dA[i] = strided_sum(part_a + i, batch, na);
   if (i < d_inner) {
-    if (dD != nullptr) {
-      float s = 0.f;
-      for (int64_t b = 0; b < batch; ++b) s += part_d[b * d_inner + i];
-      dD[i] = s;
-    }
-    if (d_dt_bias != nullptr) {
-      float s = 0.f;
-      for (int64_t b = 0; b < batch; ++b) s += part_t[b * d_inner + i];
-      d_dt_bias[i] = s;
-    }
+    if (dD != nullptr) dD[i] = strided_sum(part_d + i, batch, d_inner);
+    if (d_dt_bias != nullptr) d_dt_bias[i] = strided_sum(part_t + i, batch, d_inner);
   }
 }
 
