@@ -17,7 +17,23 @@ __global__ void __launch_bounds__(256) k_chunk_carry(const float* __restrict__ h
   if (s >= states) return;
   float hc = h0 != nullptr ? h0[s] : 0.f;
   h_entry[s] = hc;
-  for (int64_t c = 0; c + 1 < n_chunks; ++c) {
+  // The pairs of four chunks are loaded before they are combined (the loads
+  // do not depend on the state), so they are in flight together.
+  int64_t c = 0;
+  for (; c + 4 < n_chunks; c += 4) {
+    float P[4], S[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      P[j] = sumP[(c + j) * states + s];
+      S[j] = sumS[(c + j) * states + s];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hc = __builtin_fmaf(P[j], hc, S[j]);
+      h_entry[(c + j + 1) * states + s] = hc;
+    }
+  }
+  for (; c + 1 < n_chunks; ++c) {
     hc = __builtin_fmaf(sumP[c * states + s], hc, sumS[c * states + s]);
     h_entry[(c + 1) * states + s] = hc;
   }

@@ -187,7 +187,22 @@ __global__ void __launch_bounds__(256) k_bwd_lam_carry(const float* __restrict__
   if (s >= states) return;
   float v = dh_last != nullptr ? dh_last[s] : 0.f;
   lIn[(n_chunks - 1) * states + s] = v;
-  for (int64_t c = n_chunks - 1; c >= 1; --c) {
+  // Four chunks' pairs are loaded before they are combined (see k_chunk_carry).
+  int64_t c = n_chunks - 1;
+  for (; c >= 4; c -= 4) {
+    float P[4], S[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      P[j] = lP[(c - 1 - j) * states + s];
+      S[j] = lS[(c - 1 - j) * states + s];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v = __builtin_fmaf(P[j], v, S[j]);
+      lIn[(c - 1 - j) * states + s] = v;
+    }
+  }
+  for (; c >= 1; --c) {
     v = __builtin_fmaf(lP[(c - 1) * states + s], v, lS[(c - 1) * states + s]);
     lIn[(c - 1) * states + s] = v;
   }
