@@ -19,6 +19,10 @@
 //     cheapest form of the recurrence (one FMA per state per step); the work
 //     is VALU-bound, so a time-parallel scan per element would cost several
 //     times more arithmetic.
+//   * x / delta / z / y rows (and the checkpoints) go through buffer
+//     instructions: a resource per tensor over the current 8-row block, the
+//     lane's byte offset in a VGPR and the row's in an SGPR, so addressing
+//     costs no VALU (see block_rsrc below).
 //   * B_t and C_t are shared by every channel of a row: their address is
 //     wave-uniform, so they arrive through scalar loads into SGPRs (prefetched
 //     one timestep ahead) and feed the VALU as scalar operands.  No LDS
