@@ -133,32 +133,62 @@ __global__ void __launch_bounds__(64)
   const float dtb = (MODE & 1) ? dt_bias[dc] : 0.f;
   const uint32_t row_bytes = (uint32_t)(DI * (int64_t)sizeof(T));
   const uint32_t lo = (uint32_t)lc * (uint32_t)sizeof(T);
-  auto rowp = [&](const void* base, int64_t t) {
-    return uniform_ptr(reinterpret_cast<const char*>(base) + ((b * L + t) * DI + cbase) * (int64_t)sizeof(T));
+  const uint32_t blk_span = (uint32_t)kBB * row_bytes;
+  auto rs = [&](const void* base, int64_t t) {
+    return block_rsrc(reinterpret_cast<const char*>(base) + ((b * L + t) * DI + cbase) * (int64_t)sizeof(T), blk_span);
   };
   const T* Cb = C + b * L * N;
+  // Blocks run from the chunk's end backwards.  The raw delta / dy / z rows
+  // of the next (earlier) block load while the current one computes, and
+  // each step's C row is requested one step ahead through SGPRs.
+  T dn[kBB], yn[kBB], zn[kBB];
+  auto fetch = [&](int64_t t1) {
+    const int64_t t0 = max(t_lo, t1 - kBB);
+    const int nt = (int)(t1 - t0);
+    const __amdgpu_buffer_rsrc_t rd = rs(delta, t0), ry = rs(dy, t0), rz = rs(has_z ? z : delta, t0);
+#pragma unroll
+    for (int i = 0; i < kBB; ++i) {
+      const uint32_t so = (uint32_t)min(i, nt - 1) * row_bytes;  // past the end: repeat the last row
+      dn[i] = buf_ld<T>(rd, lo, so);
+      yn[i] = buf_ld<T>(ry, lo, so);
+      zn[i] = buf_ld<T>(rz, lo, so);
+    }
+  };
+  StateRow<T, N> cq;
+  if (t_hi > t_lo) {
+    fetch(t_hi);
+    cq.load(Cb + (t_hi - 1) * N);
+  }
   for (int64_t t1 = t_hi; t1 > t_lo; t1 -= kBB) {
     const int64_t t0 = max(t_lo, t1 - kBB);
     const int nt = (int)(t1 - t0);
-    const gchar* db = rowp(delta, t0);
-    const gchar* yb = rowp(dy, t0);
-    const gchar* zb = has_z ? rowp(z, t0) : db;
+    T dr[kBB], yr[kBB], zr[kBB];
+#pragma unroll
+    for (int i = 0; i < kBB; ++i) {
+      dr[i] = dn[i];
+      yr[i] = yn[i];
+      zr[i] = zn[i];
+    }
+    if (t0 > t_lo) fetch(t0);
     float dt[kBB], g[kBB];
 #pragma unroll
     for (int i = 0; i < kBB; ++i) {
-      const uint32_t o = lo + (uint32_t)min(i, nt - 1) * row_bytes;
-      float v = gld<T>(db, o);
+      float v = io_to_f32(dr[i]);
       if (MODE & 1) v = softplus(v + dtb);
       dt[i] = v;
-      const float dyv = dvalid ? gld<T>(yb, o) : 0.f;
-      const float zv = gld<T>(zb, o);
+      const float dyv = dvalid ? io_to_f32(yr[i]) : 0.f;
+      const float zv = io_to_f32(zr[i]);
       g[i] = has_z ? dyv * zv * sigmoid(zv) : dyv;
     }
 #pragma unroll
     for (int i = kBB - 1; i >= 0; --i) {
       if (i < nt) {
-        StateRow<T, N> cr;
-        cr.load(Cb + (t0 + i) * N);
+        cq.touch();
+        __builtin_amdgcn_sched_barrier(0);
+        const StateRow<T, N> cr = cq;
+        const int64_t t = t0 + i;
+        cq.load(Cb + (t > t_lo ? t - 1 : t) * N);  // at the chunk start: repeat the row
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < N; ++n) {
           const float a = hw_exp2(dt[i] * Al2[n]);
@@ -168,6 +198,7 @@ __global__ void __launch_bounds__(64)
       }
     }
   }
+  if (t_hi > t_lo) cq.touch();  // let the last row request land
   if (dvalid) {
     const int64_t o = (((int64_t)(chunk - 1) * dm.batch + b) * DI + d) * N;
 #pragma unroll
