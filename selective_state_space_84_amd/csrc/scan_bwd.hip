@@ -30,11 +30,14 @@
 //      keeping abar * h_{t-1} for its steps in VGPRs (the recurrence's inputs
 //      are not invertible in a stable way, so states are never run backwards),
 //      then walked backwards with lam in VGPRs.  B_t and C_t are wave-uniform
-//      and come through scalar loads.  dB_t and dC_t are sums over the 64
-//      channels of the wave: each lane writes its per-state terms to LDS as
-//      rows of a [state-step][lane] table and lane r then adds up row r with
-//      16-byte reads (a transpose-and-add: per state and step, one LDS write
-//      and a sixteenth of a row read, instead of a 6-level cross-lane tree).
+//      and come through scalar loads; the per-lane rows and the checkpoint
+//      go through buffer resources (lane offset in a VGPR, row offset in an
+//      SGPR), so no 64-bit address is formed on the VALU.  dB_t and dC_t are
+//      sums over the 64 channels of the wave: each lane writes its per-state
+//      terms to LDS as rows of a [state-step][lane] table and lane r then adds
+//      up row r with 16-byte reads (a transpose-and-add: per state and step,
+//      one LDS write and a sixteenth of a row read, instead of a 6-level
+//      cross-lane tree).
 //      The per-tile sums go to a partial buffer.  dA, dD and the dt-bias
 //      gradient accumulate per lane over time and are written per batch row.
 //   3. k_bwd_reduce_bc / k_bwd_reduce_params: sum the partials over tiles (dB,
@@ -84,15 +87,37 @@ __device__ __forceinline__ float zoh_coef_da(float y, float abar, float delta, f
   return __builtin_fabsf(v) < 1.0f ? small : big;
 }
 
+// Raw io values held between a load and its use: bf16 values two to a VGPR
+// (loaded into the low and high halves, widened when read), fp32 as is.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+template <typename T, int NV>
+struct RawRows;
+template <int NV>
+struct RawRows<uint16_t, NV> {
+  u16x2 v[(NV + 1) / 2];
+  __device__ __forceinline__ void set(int i, uint16_t x) { v[i >> 1][i & 1] = x; }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t w = __builtin_bit_cast(uint32_t, v[i >> 1]);
+    return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <int NV>
+struct RawRows<float, NV> {
+  float v[NV];
+  __device__ __forceinline__ void set(int i, float x) { v[i] = x; }
+  __device__ __forceinline__ float get(int i) const { return v[i]; }
+};
+
+// fp32 to the io type: bf16 with round-to-nearest-even, or unchanged.
 template <typename T>
-__device__ __forceinline__ float gld(const gchar* base, uint32_t off) {
-  return io_to_f32(*reinterpret_cast<const T __attribute__((address_space(1)))*>(base + off));
+__device__ __forceinline__ T to_io(float v);
+template <>
+__device__ __forceinline__ uint16_t to_io<uint16_t>(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
-template <typename T>
-__device__ __forceinline__ void gst(gchar* base, uint32_t off, float v) {
-  T bits;
-  io_store(&bits, v);
-  *reinterpret_cast<T __attribute__((address_space(1)))*>(base + off) = bits;
+template <>
+__device__ __forceinline__ float to_io<float>(float v) {
+  return v;
 }
 
 // Adjoint summary of chunk c >= 1: processing its steps backwards maps the
@@ -308,19 +333,17 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
   float accD = 0.f, accT = 0.f;
 
   // Addressing (as in the forward sweep): the io tensors share one layout,
-  // so a block of kBB rows is reached from one wave-uniform row pointer per
-  // tensor (SGPRs) plus per-lane 32-bit byte offsets voff[i] computed once.
+  // so a block of kBB rows is one buffer resource per tensor (SGPRs), the
+  // lane's byte offset in one VGPR and the row's offset in an SGPR.
   const int64_t cbase = (int64_t)tile * 64;
   const int lc = (int)(dc - cbase);
   const uint32_t row_bytes = (uint32_t)(DI * (int64_t)sizeof(T));
-  uint32_t voff[kBB];
-#pragma unroll
-  for (int i = 0; i < kBB; ++i) voff[i] = (uint32_t)lc * (uint32_t)sizeof(T) + (uint32_t)i * row_bytes;
+  const uint32_t lane_b = (uint32_t)lc * (uint32_t)sizeof(T);
   auto rowp = [&](const void* base, int64_t t) {
-    return uniform_ptr(reinterpret_cast<const char*>(base) + ((b * L + t) * DI + cbase) * (int64_t)sizeof(T));
+    return block_rsrc(reinterpret_cast<const char*>(base) + ((b * L + t) * DI + cbase) * (int64_t)sizeof(T),
+                      0xffffffffu);
   };
-  auto ld = [](const gchar* base, uint32_t off) { return gld<T>(base, off); };
-  auto st = [](gchar* base, uint32_t off, float v) { gst<T>(base, off, v); };
+  auto st = [&](__amdgpu_buffer_rsrc_t r, uint32_t so, float v) { buf_st(to_io<T>(v), r, lane_b, so); };
   const T* Bb = B + b * L * N;
   const T* Cb = C + b * L * N;
   float* pbc = part_bc + ((int64_t)tile * dm.batch + b) * L * (2 * N);
@@ -371,53 +394,85 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
     __syncthreads();
   };
 
+  // Row loads are requested one stage ahead of their use, into registers
+  // that are free at that point: a pass's dy and z rows and its checkpoint
+  // while the previous pass walks backwards (its h and gate terms are dead
+  // by then), and the next block's x and delta rows during the last pass of
+  // the current block.  Loads are unconditional (z falls back to x; tail
+  // lanes read a valid channel) and past a ragged end they repeat the last
+  // row, so no load waits behind a branch.
+  RawRows<T, kBB> px, pd;
+  RawRows<T, SUB> pdy, pz;
+  float ph[N];
+  const uint32_t coff = (uint32_t)lc * 4u;
+  const uint32_t crow = (uint32_t)DI * 4u;
+  auto steps_of = [&](int k) { return (int)min((int64_t)kBB, L - (int64_t)k * kBB); };
+  auto request_block = [&](int k) {
+    const int nt = steps_of(k);
+    const __amdgpu_buffer_rsrc_t xb = rowp(x, (int64_t)k * kBB);
+    const __amdgpu_buffer_rsrc_t db = rowp(delta, (int64_t)k * kBB);
+#pragma unroll
+    for (int i = 0; i < kBB; ++i) {
+      const uint32_t o = (uint32_t)min(i, nt - 1) * row_bytes;
+      px.set(i, buf_ld<T>(xb, lane_b, o));
+      pd.set(i, buf_ld<T>(db, lane_b, o));
+    }
+  };
+  auto request_pass = [&](int k, int j) {
+    const int nt = steps_of(k);
+    const __amdgpu_buffer_rsrc_t yb = rowp(dy, (int64_t)k * kBB);
+    const __amdgpu_buffer_rsrc_t zb = rowp(has_z ? (const void*)z : (const void*)x, (int64_t)k * kBB);
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+      const uint32_t o = (uint32_t)min(j * SUB + i, nt - 1) * row_bytes;
+      pdy.set(i, buf_ld<T>(yb, lane_b, o));
+      pz.set(i, buf_ld<T>(zb, lane_b, o));
+    }
+    // The checkpoint's state rows are DI floats apart: one buffer resource
+    // for the block, the lane's column in a VGPR and the row offset in an
+    // SGPR that is advanced per state (the empty asm keeps the compiler from
+    // precomputing all N row offsets, which would hold 2N SGPRs).
+    const __amdgpu_buffer_rsrc_t cpr = block_rsrc(ckpt + (b * dm.nblk + k) * N * DI + cbase, 0xffffffffu);
+    uint32_t so = 0;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      ph[n] = buf_ld<float>(cpr, coff, so);
+      so += crow;
+      asm volatile("" : "+s"(so));
+    }
+  };
+
   auto block = [&](int k) {
     const int64_t t0 = (int64_t)k * kBB;
-    const int nt = (int)min((int64_t)kBB, L - t0);
+    const int nt = steps_of(k);
     const int nsub = (nt + SUB - 1) / SUB;  // sub-blocks holding steps
-    // Row offsets; past a ragged end the loads repeat the last row.
-    const uint32_t off_last = voff[0] + (uint32_t)(nt - 1) * row_bytes;
-    auto offs = [&](int i) { return i < nt ? voff[i] : off_last; };
     float xv[kBB], dt[kBB], sg[(MODE & 1) ? kBB : 1];
-    {
-      const gchar* xb = rowp(x, t0);
-      const gchar* db = rowp(delta, t0);
 #pragma unroll
-      for (int i = 0; i < kBB; ++i) {
-        xv[i] = ld(xb, offs(i));
-        const float raw = ld(db, offs(i));
-        if (MODE & 1) {
-          const float v = raw + dtb;
-          dt[i] = softplus(v);
-          sg[i] = sigmoid(v);
-        } else {
-          dt[i] = raw;
-        }
+    for (int i = 0; i < kBB; ++i) {
+      xv[i] = px.get(i);
+      const float raw = pd.get(i);
+      if (MODE & 1) {
+        const float v = raw + dtb;
+        dt[i] = softplus(v);
+        sg[i] = sigmoid(v);
+      } else {
+        dt[i] = raw;
       }
     }
-    const gchar* cpb = uniform_ptr(ckpt + (b * dm.nblk + k) * N * DI + cbase);
-    const uint32_t coff = (uint32_t)lc * 4u;
 
 #pragma unroll
     for (int j = NSUB - 1; j >= 0; --j) {
       if (j >= nsub) continue;
       const int lo = j * SUB, hi = min(nt, lo + SUB);  // this pass covers steps [lo, hi)
-      // dy and the gate terms of this sub-block.  Loads are unconditional
-      // (zb falls back to x; tail lanes read a valid channel) and the
-      // conditions become selects, so no load waits behind a branch.
+      // dy and the gate terms of this sub-block.
       float g[SUB], dsz[SUB];
-      {
-        const gchar* yb = rowp(dy, t0);
-        const gchar* zb = has_z ? rowp(z, t0) : rowp(x, t0);
 #pragma unroll
-        for (int i = 0; i < SUB; ++i) {
-          const uint32_t o = offs(lo + i);
-          const float dyv = dvalid ? ld(yb, o) : 0.f;
-          const float zv = ld(zb, o);
-          const float s = sigmoid(zv);
-          g[i] = has_z ? dyv * zv * s : dyv;
-          dsz[i] = dyv * s * __builtin_fmaf(zv, 1.f - s, 1.f);
-        }
+      for (int i = 0; i < SUB; ++i) {
+        const float dyv = dvalid ? pdy.get(i) : 0.f;
+        const float zv = pz.get(i);
+        const float s = sigmoid(zv);
+        g[i] = has_z ? dyv * zv * s : dyv;
+        dsz[i] = dyv * s * __builtin_fmaf(zv, 1.f - s, 1.f);
       }
 
       // Forward from the checkpoint to the end of this sub-block.  Steps
@@ -427,8 +482,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
       // the compiler cannot merge the decays of different passes (keeping
       // them alive between passes would cost more VGPRs than recomputing).
       float w[SUB][N];
-      float dzo[SUB];
       float dtp[kBB];
+      const __amdgpu_buffer_rsrc_t zo = rowp(has_z ? (const void*)dz : (const void*)dx, t0);  // used only with z
 #pragma unroll
       for (int i = 0; i < kBB; ++i) {
         dtp[i] = dt[i];
@@ -437,7 +492,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
       {
         float h[N];
 #pragma unroll
-        for (int n = 0; n < N; ++n) h[n] = gld<float>(cpb + (int64_t)n * DI * 4, coff);
+        for (int n = 0; n < N; ++n) h[n] = ph[n];
 #pragma unroll
         for (int i = 0; i < lo; ++i) {
           StateRow<T, N> br, cr;
@@ -483,21 +538,24 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
                 acc = __builtin_fmaf(cr.get(n), h[n], acc);
                 red[(s * N + n) * kRedStride + lane] = g[ii] * h[n];
               }
-              dzo[ii] = acc * dsz[ii];
+              if (has_z && dvalid) st(zo, (uint32_t)i * row_bytes, acc * dsz[ii]);
             }
           }
           reduce(t0, lo + g0, nt, N);
         }
       }
-      if (has_z && dvalid) {
-        gchar* ob = rowp(dz, t0);
-#pragma unroll
-        for (int ii = 0; ii < SUB; ++ii)
-          if (lo + ii < hi) st(ob, voff[lo + ii], dzo[ii]);
+
+      // The next stage's rows: this block's next pass, or the next block.
+      if (j > 0) {
+        request_pass(k, j - 1);
+      } else if (k > kb) {
+        request_block(k - 1);
+        request_pass(k - 1, NSUB - 1);
       }
 
       // Backward through this sub-block.
-      float dxo[SUB], ddo[SUB];
+      const __amdgpu_buffer_rsrc_t xo = rowp(dx, t0);
+      const __amdgpu_buffer_rsrc_t po = rowp(ddelta, t0);
 #pragma unroll
       for (int g0 = SUB - GS; g0 >= 0; g0 -= GS) {
         if (lo + g0 >= hi) continue;
@@ -542,32 +600,27 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
                 lam[n] *= hw_exp2(dti * Al2[n]);
               }
             }
-            dxo[ii] = (MODE & kExactZoh) ? __builtin_fmaf(g[ii], Dv, sb) : __builtin_fmaf(g[ii], Dv, dti * sb);
+            const float dxv =
+                (MODE & kExactZoh) ? __builtin_fmaf(g[ii], Dv, sb) : __builtin_fmaf(g[ii], Dv, dti * sb);
             float ddt = __builtin_fmaf(dd, kLn2, xv[i] * ((MODE & kExactZoh) ? sa : sb));
             if (MODE & 1) ddt *= sg[i];
             accT += ddt;
-            ddo[ii] = ddt;
             accD = __builtin_fmaf(g[ii], xv[i], accD);
+            if (dvalid) {
+              st(xo, (uint32_t)i * row_bytes, dxv);
+              st(po, (uint32_t)i * row_bytes, ddt);
+            }
           }
         }
         reduce(t0, lo + g0, nt, 0);
-      }
-      if (dvalid) {
-        gchar* ob = rowp(dx, t0);
-        gchar* pb = rowp(ddelta, t0);
-#pragma unroll
-        for (int ii = 0; ii < SUB; ++ii) {
-          if (lo + ii < hi) {
-            st(ob, voff[lo + ii], dxo[ii]);
-            st(pb, voff[lo + ii], ddo[ii]);
-          }
-        }
       }
     }
   };
 
   if (ke > kb) {
     issue((int64_t)(ke - 1) * kBB);
+    request_block(ke - 1);
+    request_pass(ke - 1, (steps_of(ke - 1) + SUB - 1) / SUB - 1);
     for (int k = ke - 1; k >= kb; --k) block(k);
     // Let the last row request land before the wave ends.
     bq.touch();
