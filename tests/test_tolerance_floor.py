@@ -4,7 +4,7 @@ A float32 emulation (numpy) of the kernel's operation order, with correctly
 rounded exp2 / log2, is compared with the fp64 oracle under the floored
 metric.  It shows that
 
-  * the plain scan stays inside the benchmark spec's 1e-5 fp32 gate (with little
+  * the plain scan stays inside the 1e-5 fp32 parity gate (with little
     room at d_state 64: ~9e-6 on this case),
   * the softplus-step variant reaches ~1.2e-5 on some shapes even with
     correctly rounded transcendentals, so its fp32 gate must be looser:
