@@ -119,18 +119,34 @@ __global__ void __launch_bounds__(kUpdBlock)
   LaneStates<SPL>::load(A + dc * N + s0, al);
   const float Dv = D != nullptr ? D[dc] : 0.f;
   const float dtb = (MODE & 1) ? dt_bias[dc] : 0.f;
+  // All rows' loads are issued before any row is computed or stored (a row
+  // past the batch reads row b0 and stores nothing), so a thread has every
+  // load of its R rows in flight at once; the per-channel inputs go first,
+  // since in a decode loop they are the cold data (the state, rewritten every
+  // step, is more likely to be found in the on-package cache).
+  // Measured at 256 x 5120 x 16 bf16 with fresh inputs each step: 36.9 us
+  // per step with each row loaded after the previous row's store, 35.3 us
+  // this way.
+  float hv[R][SPL], Bv[R][SPL], Cv[R][SPL], xr[R], dr[R], zr[R];
+  bool rv[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t bq = b0 + r * rows;
+    rv[r] = r == 0 || bq < batch;
+    const int64_t b = rv[r] ? bq : b0;
+    const int64_t io = b * d_inner + dc;
+    xr[r] = io_to_f32(x[io]);
+    dr[r] = io_to_f32(delta[io]);
+    zr[r] = z != nullptr ? io_to_f32(z[io]) : 0.f;
+    load_row<SPL>(B + b * N + s0, Bv[r]);
+    load_row<SPL>(C + b * N + s0, Cv[r]);
+    LaneStates<SPL>::load(h + (b * d_inner + dc) * N + s0, hv[r]);
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t b = b0 + r * rows;
-    if (R > 1 && b >= batch) break;  // uniform across the workgroup
-    float* hp = h + (b * d_inner + dc) * N + s0;
-    float hv[SPL], Bv[SPL], Cv[SPL];
-    LaneStates<SPL>::load(hp, hv);
-    load_row<SPL>(B + b * N + s0, Bv);
-    load_row<SPL>(C + b * N + s0, Cv);
-    const int64_t io = b * d_inner + dc;
-    const float xv = io_to_f32(x[io]);
-    float dv = io_to_f32(delta[io]);
+    const float xv = xr[r];
+    float dv = dr[r];
     if (MODE & 1) dv = softplus(dv + dtb);
     const float wx = dv * xv;
     float acc = 0.f;
@@ -140,26 +156,27 @@ __global__ void __launch_bounds__(kUpdBlock)
       const float ab = hw_exp2(yv);
       if (MODE & 2) {
         const float coef = zoh_coef(yv, ab, dv, 1.0f / al[n]);
-        hv[n] = __builtin_fmaf(coef, xv * Bv[n], ab * hv[n]);
+        hv[r][n] = __builtin_fmaf(coef, xv * Bv[r][n], ab * hv[r][n]);
       } else {
-        hv[n] = __builtin_fmaf(ab, hv[n], wx * Bv[n]);
+        hv[r][n] = __builtin_fmaf(ab, hv[r][n], wx * Bv[r][n]);
       }
-      acc = __builtin_fmaf(Cv[n], hv[n], acc);
+      acc = __builtin_fmaf(Cv[r][n], hv[r][n], acc);
     }
     acc = group_sum<LPC>(acc);
-    if (valid) {
-      LaneStates<SPL>::store(hp, hv);
+    if (valid && rv[r]) {
+      LaneStates<SPL>::store(h + (b * d_inner + dc) * N + s0, hv[r]);
       if (sub == 0) {
         float v = __builtin_fmaf(Dv, xv, acc);
-        if (z != nullptr) v *= silu(io_to_f32(z[io]));
-        io_store(y + io, v);
+        if (z != nullptr) v *= silu(zr[r]);
+        io_store(y + b * d_inner + dc, v);
       }
     }
   }
 }
 
 // Batch rows per thread: A, D and dt_bias loads are shared by this many rows
-// (measured at 256 x 5120 x 16 bf16: 2 rows 37.1 us, 1 row 38.1, 4 rows 38.5).
+// (measured at 256 x 5120 x 16 bf16 with the loads issued first: 1 row
+// 38.4 us, 2 rows 35.9, 4 rows 35.9).
 constexpr int kUpdRows = 2;
 
 template <typename T, int SPL, int LPC, int MODE>
