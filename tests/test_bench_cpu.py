@@ -1,0 +1,42 @@
+"""Host-side parts of bench.py that run without a GPU: the one-GPU contract,
+the algorithmic byte count behind the HBM figure, and the rule that a
+counter-derived traffic figure is reported only for the sources it was
+measured on."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(REPO, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_algorithmic_scan_bytes():
+    # bf16 io, no h0, with h_last: x, delta, z read and y written (2 B each),
+    # B and C rows (2 B per state), A and D, and the final state.
+    b, L, d, n = 32, 4096, 4096, 16
+    want = 4 * b * L * d * 2 + 2 * b * L * n * 2 + d * n * 4 + d * 4 + b * d * n * 4
+    assert bench.algorithmic_scan_bytes(b, L, d, n, 2, False, True) == want == 4312023040
+    # An initial state adds one more state read.
+    assert bench.algorithmic_scan_bytes(b, L, d, n, 2, True, True) == want + b * d * n * 4
+
+
+def test_traffic_follows_the_kernel_sources():
+    sha = bench._kernel_source_sha("scan")
+    assert len(sha) == 16 and sha != bench._kernel_source_sha("decode")
+    assert bench._traffic("mamba-1.4b-layer", "0" * 16) is None
+    assert bench._traffic("no-such-workload", sha) is None
+    got = bench._traffic("mamba-1.4b-layer", sha)
+    if got is None:
+        pytest.skip("the scan kernel changed since its traffic counters were taken")
+    # Measured traffic sits within a few percent of the algorithmic bytes.
+    assert abs(got / 4312023040 - 1) < 0.05
