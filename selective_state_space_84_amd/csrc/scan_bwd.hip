@@ -442,10 +442,14 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
     }
   };
 
+  // The exact-ZOH variant (one wave per SIMD, its registers already full)
+  // requests each stage's rows at the start of that stage instead.
+  constexpr bool kEarly = (MODE & kExactZoh) == 0;
   auto block = [&](int k) {
     const int64_t t0 = (int64_t)k * kBB;
     const int nt = steps_of(k);
     const int nsub = (nt + SUB - 1) / SUB;  // sub-blocks holding steps
+    if (!kEarly) request_block(k);
     float xv[kBB], dt[kBB], sg[(MODE & 1) ? kBB : 1];
 #pragma unroll
     for (int i = 0; i < kBB; ++i) {
@@ -464,6 +468,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
     for (int j = NSUB - 1; j >= 0; --j) {
       if (j >= nsub) continue;
       const int lo = j * SUB, hi = min(nt, lo + SUB);  // this pass covers steps [lo, hi)
+      if (!kEarly) request_pass(k, j);
       // dy and the gate terms of this sub-block.
       float g[SUB], dsz[SUB];
 #pragma unroll
@@ -546,11 +551,13 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
       }
 
       // The next stage's rows: this block's next pass, or the next block.
-      if (j > 0) {
-        request_pass(k, j - 1);
-      } else if (k > kb) {
-        request_block(k - 1);
-        request_pass(k - 1, NSUB - 1);
+      if (kEarly) {
+        if (j > 0) {
+          request_pass(k, j - 1);
+        } else if (k > kb) {
+          request_block(k - 1);
+          request_pass(k - 1, NSUB - 1);
+        }
       }
 
       // Backward through this sub-block.
@@ -619,8 +626,10 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
 
   if (ke > kb) {
     issue((int64_t)(ke - 1) * kBB);
-    request_block(ke - 1);
-    request_pass(ke - 1, (steps_of(ke - 1) + SUB - 1) / SUB - 1);
+    if (kEarly) {
+      request_block(ke - 1);
+      request_pass(ke - 1, (steps_of(ke - 1) + SUB - 1) / SUB - 1);
+    }
     for (int k = ke - 1; k >= kb; --k) block(k);
     // Let the last row request land before the wave ends.
     bq.touch();
