@@ -87,8 +87,9 @@ __device__ __forceinline__ float zoh_coef_da(float y, float abar, float delta, f
   return __builtin_fabsf(v) < 1.0f ? small : big;
 }
 
-// Raw io values held between a load and its use: bf16 values two to a VGPR
-// (loaded into the low and high halves, widened when read), fp32 as is.
+// Raw io rows of one stage: bf16 values two to a dword (widened when read;
+// the compiler folds the packing away when the values are used right after
+// the load), fp32 as is.
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 template <typename T, int NV>
 struct RawRows;
@@ -394,13 +395,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
     __syncthreads();
   };
 
-  // Row loads are requested one stage ahead of their use, into registers
-  // that are free at that point: a pass's dy and z rows and its checkpoint
-  // while the previous pass walks backwards (its h and gate terms are dead
-  // by then), and the next block's x and delta rows during the last pass of
-  // the current block.  Loads are unconditional (z falls back to x; tail
-  // lanes read a valid channel) and past a ragged end they repeat the last
-  // row, so no load waits behind a branch.
+  // Each stage requests its rows when it starts: a block its x and delta
+  // rows, a pass its dy and z rows and its checkpoint.  Requesting them one
+  // stage earlier, into registers free at that point, kept more values live
+  // and measured slower at two waves per SIMD.  Loads are unconditional (z
+  // falls back to x; tail lanes read a valid channel) and past a ragged end
+  // they repeat the last row, so no load waits behind a branch.
   RawRows<T, kBB> px, pd;
   RawRows<T, SUB> pdy, pz;
   float ph[N];
@@ -442,14 +442,11 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
     }
   };
 
-  // The exact-ZOH variant (one wave per SIMD, its registers already full)
-  // requests each stage's rows at the start of that stage instead.
-  constexpr bool kEarly = (MODE & kExactZoh) == 0;
   auto block = [&](int k) {
     const int64_t t0 = (int64_t)k * kBB;
     const int nt = steps_of(k);
     const int nsub = (nt + SUB - 1) / SUB;  // sub-blocks holding steps
-    if (!kEarly) request_block(k);
+    request_block(k);
     float xv[kBB], dt[kBB], sg[(MODE & 1) ? kBB : 1];
 #pragma unroll
     for (int i = 0; i < kBB; ++i) {
@@ -468,7 +465,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
     for (int j = NSUB - 1; j >= 0; --j) {
       if (j >= nsub) continue;
       const int lo = j * SUB, hi = min(nt, lo + SUB);  // this pass covers steps [lo, hi)
-      if (!kEarly) request_pass(k, j);
+      request_pass(k, j);
       // dy and the gate terms of this sub-block.
       float g[SUB], dsz[SUB];
 #pragma unroll
@@ -550,16 +547,6 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
         }
       }
 
-      // The next stage's rows: this block's next pass, or the next block.
-      if (kEarly) {
-        if (j > 0) {
-          request_pass(k, j - 1);
-        } else if (k > kb) {
-          request_block(k - 1);
-          request_pass(k - 1, NSUB - 1);
-        }
-      }
-
       // Backward through this sub-block.
       const __amdgpu_buffer_rsrc_t xo = rowp(dx, t0);
       const __amdgpu_buffer_rsrc_t po = rowp(ddelta, t0);
@@ -626,10 +613,6 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_swe
 
   if (ke > kb) {
     issue((int64_t)(ke - 1) * kBB);
-    if (kEarly) {
-      request_block(ke - 1);
-      request_pass(ke - 1, (steps_of(ke - 1) + SUB - 1) / SUB - 1);
-    }
     for (int k = ke - 1; k >= kb; --k) block(k);
     // Let the last row request land before the wave ends.
     bq.touch();
