@@ -277,16 +277,11 @@ constexpr int bwd_sub() {
   return N * kBB <= 64 ? kBB : 64 / N;
 }
 
-// Waves per SIMD the sweep is compiled for: two, except with the exact ZOH
-// at 16 states, whose extra per-state terms (1/a, the coefficient and its
-// derivative) do not fit 256 VGPRs next to the kept w values.
-template <int N, int MODE>
-constexpr int bwd_sweep_waves() {
-  return ((MODE & kExactZoh) && N >= 16) ? 1 : 2;
-}
-
+// Compiled for two waves per SIMD (256 VGPRs).  The exact-ZOH variant at 16
+// states spills ~130 B per lane at that size and is still faster than at one
+// wave per SIMD without spills.
 template <typename T, int N, int MODE>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_sweep_waves<N, MODE>())))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     k_bwd_sweep(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
                 const T* __restrict__ B, const T* __restrict__ C, const float* __restrict__ D,
                 const T* __restrict__ z, const T* __restrict__ dy, const float* __restrict__ dh_last,
