@@ -220,6 +220,17 @@ int ssm_state_update_ex(float* h, const void* x_t, const void* delta_t, const fl
 size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state);
 
 /*
+ * Workspace bytes ssm_scan_bwd needs when ckpt_given is 1, i.e. the call
+ * passes the checkpoints a forward call saved: the backward pass then
+ * computes no checkpoints of its own and needs no room for them (about a
+ * third of ssm_scan_bwd_workspace_size at d_state 16).  With ckpt_given 0 it
+ * equals ssm_scan_bwd_workspace_size.  Returns (size_t)-1 for invalid sizes
+ * or a ckpt_given other than 0 or 1.  Pure host computation.
+ */
+size_t ssm_scan_bwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                      int32_t ckpt_given);
+
+/*
  * Gradient of ssm_scan_fwd (the training backward pass).  Training
  * back-propagates through the scan along time, recomputing intermediate
  * states from a few kept ones ("SSMs for long-document QA"
@@ -254,8 +265,9 @@ size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inne
  *                 (exp(delta a) - 1)/a is differentiated in both delta (its
  *                 derivative is abar) and a.
  *   d_state     : 2, 4, 8 or 16.
- *   workspace   : at least ssm_scan_bwd_workspace_size() bytes, 256-byte
- *                 aligned; contents on entry ignored.
+ *   workspace   : at least ssm_scan_bwd_workspace_size() bytes (or
+ *                 ssm_scan_bwd_workspace_size_ex(..., 1) when ckpt is given),
+ *                 256-byte aligned; contents on entry ignored.
  * Every output is overwritten, not accumulated.  Outputs must not overlap
  * each other, any input or the workspace.  Sums over channels, time and
  * batch rows are taken in a fixed order: results are bitwise reproducible

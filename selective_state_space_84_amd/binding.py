@@ -56,6 +56,7 @@ SIGNATURES = {
     "ssm_state_update": ([_P] * 9 + [_I64] * 3 + [_I32, _P], ctypes.c_int),
     "ssm_state_update_ex": ([_P] * 9 + [_I64] * 3 + [_I32, _U32, _P, _P], ctypes.c_int),
     "ssm_scan_bwd_workspace_size": ([_I64, _I64, _I64, _I64], _SZ),
+    "ssm_scan_bwd_workspace_size_ex": ([_I64, _I64, _I64, _I64, _I32], _SZ),
     "ssm_scan_ckpt_bytes": ([_I64, _I64, _I64, _I64], _SZ),
     "ssm_scan_bwd": ([_P] * 21 + [_I64] * 4 + [_I32, _U32, _P, _SZ, _P], ctypes.c_int),
     "ssm_ssd_fwd": ([_P] * 10 + [_I64] * 6 + [_I32, _U32, _P, _P], ctypes.c_int),
@@ -208,10 +209,11 @@ def ssm_state_update(h, x_t, delta_t, A, B_t, C_t, D=None, z_t=None, *, y_t=None
     return y_t
 
 
-def scan_bwd_workspace_size(batch, seqlen, d_inner, d_state) -> int:
-    n = load_library().ssm_scan_bwd_workspace_size(batch, seqlen, d_inner, d_state)
+def scan_bwd_workspace_size(batch, seqlen, d_inner, d_state, ckpt_given=False) -> int:
+    """Backward workspace bytes; smaller when the forward call's checkpoints are passed."""
+    n = load_library().ssm_scan_bwd_workspace_size_ex(batch, seqlen, d_inner, d_state, 1 if ckpt_given else 0)
     if n == ctypes.c_size_t(-1).value:
-        raise SsmError(SSM_ERR_BAD_DIM, "ssm_scan_bwd_workspace_size")
+        raise SsmError(SSM_ERR_BAD_DIM, "ssm_scan_bwd_workspace_size_ex")
     return n
 
 
@@ -250,7 +252,7 @@ def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None
         g["dh0"] = torch.empty((batch, d_inner, d_state), **f32)
     if (flags & SSM_FLAG_DELTA_SOFTPLUS) and "d_dt_bias" not in g:
         g["d_dt_bias"] = torch.empty((d_inner,), **f32)
-    ws_bytes = scan_bwd_workspace_size(batch, seqlen, d_inner, d_state)
+    ws_bytes = scan_bwd_workspace_size(batch, seqlen, d_inner, d_state, ckpt_given=ckpt is not None)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -279,7 +279,7 @@ int update_impl(float* h, const void* x_t, const void* delta_t, const float* A, 
 bool bwd_d_state_ok(int64_t n) { return n == 2 || n == 4 || n == 8 || n == 16; }
 
 // Floats of backward workspace, or -1 when a size overflows.
-int64_t bwd_workspace_floats(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+int64_t bwd_workspace_floats(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, bool ckpt_given) {
   const int64_t tiles = (d_inner + 63) / 64;
   const int64_t nblk = (seqlen + ssm::kBwdBlock - 1) / ssm::kBwdBlock;
   int64_t a, b, c;
@@ -289,7 +289,8 @@ int64_t bwd_workspace_floats(int64_t batch, int64_t seqlen, int64_t d_inner, int
   if (!mul3(batch, d_inner, d_state, &c)) return -1;
   if (a > INT64_MAX / 8 || b > INT64_MAX / 8 || c > INT64_MAX / 8) return -1;
   int64_t total;
-  ssm::bwd_workspace_layout(nullptr, batch, seqlen, d_inner, d_state, ssm::bwd_plan(batch, seqlen, d_inner), &total);
+  ssm::bwd_workspace_layout(nullptr, batch, seqlen, d_inner, d_state, ssm::bwd_plan(batch, seqlen, d_inner), ckpt_given,
+                            &total);
   return total;
 }
 
@@ -360,7 +361,7 @@ int bwd_impl(const void* x, const void* delta, const float* A, const void* B, co
       if (overlap(outs[o], outb[o], outs[k], outb[k])) return SSM_ERR_ALIAS;
   }
 
-  const int64_t floats = bwd_workspace_floats(batch, seqlen, d_inner, d_state);
+  const int64_t floats = bwd_workspace_floats(batch, seqlen, d_inner, d_state, ckpt != nullptr);
   if (floats < 0) return SSM_ERR_BAD_DIM;
   const int64_t need = floats * 4;
   if (need > 0) {
@@ -380,7 +381,8 @@ int bwd_impl(const void* x, const void* delta, const float* A, const void* B, co
   if (d_inner == 0) return SSM_OK;
   float* ws = static_cast<float*>(workspace);
   const ssm::BwdPlan plan = ssm::bwd_plan(batch, seqlen, d_inner);
-  const ssm::BwdWorkspace lay = ssm::bwd_workspace_layout(ws, batch, seqlen, d_inner, d_state, plan, nullptr);
+  const ssm::BwdWorkspace lay =
+      ssm::bwd_workspace_layout(ws, batch, seqlen, d_inner, d_state, plan, ckpt != nullptr, nullptr);
   ssm::BwdLaunch p{x, delta, A, B, C, D, z, h0, dt_bias, dy, dh_last, ckpt, dx, ddelta, dA, dB, dC, dD, dz, dh0,
                    d_dt_bias, flags, batch, seqlen, d_inner, (int32_t)d_state, io_dtype == SSM_DTYPE_BF16,
                    static_cast<hipStream_t>(stream)};
@@ -487,11 +489,17 @@ int ssm_conv1d_update(float* state, const void* x_t, const float* w, const float
 }
 
 
-size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+size_t ssm_scan_bwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                      int32_t ckpt_given) {
   if (check_dims(batch, seqlen, d_inner, d_state) != SSM_OK || !bwd_d_state_ok(d_state)) return (size_t)-1;
-  const int64_t floats = bwd_workspace_floats(batch, seqlen, d_inner, d_state);
+  if (ckpt_given != 0 && ckpt_given != 1) return (size_t)-1;
+  const int64_t floats = bwd_workspace_floats(batch, seqlen, d_inner, d_state, ckpt_given == 1);
   if (floats < 0) return (size_t)-1;
   return (size_t)floats * 4;
+}
+
+size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  return ssm_scan_bwd_workspace_size_ex(batch, seqlen, d_inner, d_state, 0);
 }
 
 size_t ssm_scan_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {

@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(64)
 #pragma unroll
     for (int i = 0; i < kBB; ++i) {
       float v = io_to_f32(dr[i]);
-      if (MODE & 1) v = softplus(v + dtb);
+      if (MODE & 1) v = softplus(v, dtb);
       dt[i] = v;
       const float dyv = dvalid ? io_to_f32(yr[i]) : 0.f;
       const float zv = io_to_f32(zr[i]);
@@ -449,7 +449,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
       const float raw = pd.get(i);
       if (MODE & 1) {
         const float v = raw + dtb;
-        dt[i] = softplus(v);
+        dt[i] = softplus(raw, dtb);
         sg[i] = sigmoid(v);
       } else {
         dt[i] = raw;
@@ -793,33 +793,37 @@ BwdPlan bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner) {
 }
 
 BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                                  const BwdPlan& plan, int64_t* total_floats) {
+                                  const BwdPlan& plan, bool ckpt_given, int64_t* total_floats) {
   auto up = [](int64_t v) { return (v + 63) / 64 * 64; };  // 256-byte sections
   const int64_t tiles = (d_inner + 63) / 64;
   const int64_t nblk = (seqlen + kBB - 1) / kBB;
   const int64_t nch = plan.n_chunks;
   const int64_t states = batch * d_inner * d_state;
-  const int64_t n_ck = up(batch * nblk * d_state * d_inner);
+  const int64_t n_ck = ckpt_given ? 0 : up(batch * nblk * d_state * d_inner);
   const int64_t n_bc = up(tiles * batch * seqlen * 2 * d_state);
   const int64_t n_a = up(nch * states);
   const int64_t n_d = up(nch * batch * d_inner);
   const int64_t n_sum = nch > 1 ? up((nch - 1) * states) : 0;
   const int64_t n_ent = nch > 1 ? up(nch * states) : 0;
+  // Forward chunk summaries and entry states: only to compute checkpoints.
+  const int64_t n_fsum = ckpt_given ? 0 : n_sum;
+  const int64_t n_fent = ckpt_given ? 0 : n_ent;
   BwdWorkspace ws{};
   if (base != nullptr) {
-    ws.ckpt = base;
-    ws.part_bc = ws.ckpt + n_ck;
+    ws.ckpt = ckpt_given ? nullptr : base;
+    ws.part_bc = base + n_ck;
     ws.part_a = ws.part_bc + n_bc;
     ws.part_d = ws.part_a + n_a;
     ws.part_t = ws.part_d + n_d;
-    ws.fP = ws.part_t + n_d;
-    ws.fS = ws.fP + n_sum;
-    ws.fH = ws.fS + n_sum;
-    ws.lP = ws.fH + n_ent;
+    float* f = ws.part_t + n_d;
+    ws.fP = ckpt_given ? nullptr : f;
+    ws.fS = ckpt_given ? nullptr : f + n_fsum;
+    ws.fH = ckpt_given ? nullptr : f + 2 * n_fsum;
+    ws.lP = f + 2 * n_fsum + n_fent;
     ws.lS = ws.lP + n_sum;
     ws.lIn = ws.lS + n_sum;
   }
-  if (total_floats != nullptr) *total_floats = n_ck + n_bc + n_a + 2 * n_d + 4 * n_sum + 2 * n_ent;
+  if (total_floats != nullptr) *total_floats = n_ck + n_bc + n_a + 2 * n_d + 2 * n_fsum + n_fent + 2 * n_sum + n_ent;
   return ws;
 }
 

@@ -281,7 +281,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
       float d = 0.f;
       if (lane < nt_) {
         d = lo_f32(dcur);
-        if (MODE & 1) d = softplus(d + dtb);
+        if (MODE & 1) d = softplus(d, dtb);
       }
       const float l = scan32(d * Al2);
       const float lq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), kQ - 1));

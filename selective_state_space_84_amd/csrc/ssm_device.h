@@ -24,24 +24,53 @@ __device__ __forceinline__ float hw_exp2(float v) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
 __device__ __forceinline__ float hw_log2(float v) { return __builtin_amdgcn_logf(v); }
 
-// softplus(v) = log(1 + e^v).
-//  * e^v = 2^(v log2 e): the rounding of the product v * log2(e) (|v| up to
-//    ~10 here) would cost ~5e-7 relative in e^v, so the product is split into
-//    hi + lo (one FMA, plus log2(e)'s own low part) and e^v is corrected to
-//    first order in lo.
-//  * With u = 1 + e^v rounded, log(u) loses the low bits of a small e^v; the
-//    factor e^v / (u - 1) restores them (Kahan's log1p rearrangement).
-// For v > 20 the result is v to fp32 precision (and e^v may overflow).
+// softplus(raw + bias) = log(1 + e^v), v = raw + bias, to about 2 ulp of the
+// value at the exact sum.  softplus(v) ~ e^v for v < 0 has relative
+// condition number |v|, so the rounding of raw + bias alone would cost ~|v|/2
+// ulp; the sum is therefore kept as vh + vl (Knuth's two-sum, exact).  Then
+// softplus(v) = max(v, 0) + log1p(t) with t = e^-|v| in (0, 1]:
+//  * t = 2^(a log2 e), a = -|v|: the exponent is split into yh + yl (the
+//    rounding of yh, log2(e)'s low part and vl's share), so t = th + tl with
+//    th = 2^yh from the hardware unit and tl = th * yl * ln2 (first order);
+//  * log1p(t) = 2 atanh(s) with s = t / (2 + t) <= 1/3 (the atanh series
+//    of log((1 + s) / (1 - s))): s0 = th / d with d = 2 + th rounded, then one
+//    residual step on (th + tl) - s0 (d + dl + tl), dl = d's rounding error
+//    (exact), gives s to ~0.5 ulp; the series tail 2s (s^2/3 + ... + s^14/15)
+//    is below 4% of the result, so its own rounding hardly shows.
+// For |v| beyond 1e30 the low part is dropped and below -200 the exponent is
+// clamped (+inf stays +inf, -inf gives 0); NaN propagates.  Results below
+// fp32's normal range flush towards zero.
 constexpr float kLog2eLo = 1.925963e-8f;  // log2(e) - (float)log2(e)
-__device__ __forceinline__ float softplus(float v) {
-  const float yh = v * kLog2e;
-  const float yl = __builtin_fmaf(v, kLog2e, -yh) + v * kLog2eLo;
-  float e = hw_exp2(yh);
-  e = __builtin_fmaf(e, yl * kLn2, e);
-  const float u = 1.0f + e;
-  const float um1 = u - 1.0f;
-  const float r = um1 == 0.0f ? e : hw_log2(u) * kLn2 * (e * hw_rcp(um1));
-  return v > 20.0f ? v : r;
+__device__ __forceinline__ float softplus(float raw, float bias) {
+  const float vh = raw + bias;
+  const float bb = vh - raw;
+  const float vl = __builtin_fabsf(vh) < 1e30f ? (raw - (vh - bb)) + (bias - bb) : 0.0f;
+  const bool pos = vh > 0.0f;
+  float a = pos ? -vh : vh;
+  a = a < -200.0f ? -200.0f : a;  // e^-200 is 0 in fp32; keeps -inf out of the exponent (NaN passes)
+  const float al = pos ? -vl : vl;
+  const float yh = a * kLog2e;
+  const float yl = __builtin_fmaf(a, kLog2e, -yh) + __builtin_fmaf(al, kLog2e, a * kLog2eLo);
+  const float th = hw_exp2(yh);
+  const float tl = th * (yl * kLn2);
+  const float d = 2.0f + th;
+  const float dl = th - (d - 2.0f);
+  const float r = hw_rcp(d);
+  const float s0 = th * r;
+  float e = __builtin_fmaf(-s0, d, th);
+  e = __builtin_fmaf(-s0, dl + tl, e + tl);
+  const float s = __builtin_fmaf(e, r, s0);
+  const float z = s * s;
+  float q = 1.0f / 15.0f;
+  q = __builtin_fmaf(q, z, 1.0f / 13.0f);
+  q = __builtin_fmaf(q, z, 1.0f / 11.0f);
+  q = __builtin_fmaf(q, z, 1.0f / 9.0f);
+  q = __builtin_fmaf(q, z, 1.0f / 7.0f);
+  q = __builtin_fmaf(q, z, 1.0f / 5.0f);
+  q = __builtin_fmaf(q, z, 1.0f / 3.0f);
+  const float s2 = s + s;
+  const float lp = __builtin_fmaf(s2, z * q, s2);
+  return pos ? vh + (lp + vl) : lp;
 }
 
 // v * sigmoid(v) = v / (1 + exp(-v)).  For v -> -inf the exponential
@@ -50,21 +79,27 @@ __device__ __forceinline__ float silu(float v) { return v * hw_rcp(1.0f + hw_exp
 
 // Coefficient of B*x in the exact zero-order hold, (exp(delta a) - 1) / a,
 // from y = delta * a * log2(e), abar = 2^y and inv_a = 1/a:
-//   |y| < 1/4: delta * phi, phi = (e^v - 1)/v = sum_k v^k/(k+1)! with v = y ln 2,
-//              to 4th order (truncation < 3e-7 relative); this also covers a = 0;
-//   otherwise: (abar - 1) * inv_a, where abar's rounding is small against
-//              abar - 1 (|abar - 1| > 0.16).
-// Relative error below ~5e-7 over the whole range.
-constexpr float kZoh1 = 0.3465736f;    // ln2 / 2!
-constexpr float kZoh2 = 0.0800755f;    // ln2^2 / 3!
-constexpr float kZoh3 = 0.013876027f;  // ln2^3 / 4!
-constexpr float kZoh4 = 0.0019236258f; // ln2^4 / 5!
+//   |y| < 1/2: delta * phi, phi = (e^v - 1)/v = sum_k v^k/(k+1)! with v = y ln 2,
+//              to 6th order (truncation < 2e-8 relative); this also covers a = 0;
+//   otherwise: (abar - 1) * inv_a, where |abar - 1| > 0.29, so abar's error
+//              (under 0.8 ulp) grows at most ~2.4x.
+// Relative error about 3 ulp or less over the whole range.
+constexpr float kZoh1 = 0.34657359f;     // ln2 / 2!
+constexpr float kZoh2 = 0.080075503f;    // ln2^2 / 3!
+constexpr float kZoh3 = 0.013876027f;    // ln2^3 / 4!
+constexpr float kZoh4 = 0.0019236258f;   // ln2^4 / 5!
+constexpr float kZoh5 = 2.2222597e-4f;   // ln2^5 / 6!
+constexpr float kZoh6 = 2.2005043e-5f;   // ln2^6 / 7!
 __device__ __forceinline__ float zoh_coef(float y, float abar, float delta, float inv_a) {
-  const float phi =
-      __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(__builtin_fmaf(y, kZoh4, kZoh3), y, kZoh2), y, kZoh1), y, 1.0f);
+  float p = __builtin_fmaf(y, kZoh6, kZoh5);
+  p = __builtin_fmaf(p, y, kZoh4);
+  p = __builtin_fmaf(p, y, kZoh3);
+  p = __builtin_fmaf(p, y, kZoh2);
+  p = __builtin_fmaf(p, y, kZoh1);
+  const float phi = __builtin_fmaf(p, y, 1.0f);
   const float small = delta * phi;
   const float big = __builtin_fmaf(abar, inv_a, -inv_a);
-  return __builtin_fabsf(y) < 0.25f ? small : big;
+  return __builtin_fabsf(y) < 0.5f ? small : big;
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X

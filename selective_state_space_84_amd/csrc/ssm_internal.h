@@ -113,8 +113,12 @@ struct BwdLaunch {
   hipStream_t stream;
 };
 
-// Steps per checkpoint block of the backward pass.
-constexpr int kBwdBlock = 8;
+// Steps per checkpoint block of the backward pass.  The forward sweep writes
+// the checkpoints ([batch][ceil(seqlen/8)][d_state][d_inner], the state
+// before every block) with its own block length, and ssm_scan_ckpt_bytes
+// sizes them the same way: the two must stay equal.
+constexpr int kBwdBlock = kTimeBlock;
+static_assert(kBwdBlock == kTimeBlock, "forward checkpoints and backward blocks share one block length");
 
 // Sequence chunks of the backward pass: (chunk_len, n_chunks), chunk_len a
 // multiple of kBwdBlock.  Chunks are used only when channels alone leave the
@@ -127,7 +131,9 @@ struct BwdPlan {
 BwdPlan bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner);
 
 // Sections of the backward workspace (floats, each 256-byte aligned), with
-// S = batch * d_inner * d_state states and c = n_chunks:
+// S = batch * d_inner * d_state states and c = n_chunks.  When the caller
+// passes the forward call's checkpoints (ckpt_given), the sections that only
+// serve to compute them (ckpt, fP, fS, fH) are left out.
 //   ckpt    [batch][ceil(seqlen/8)][d_state][d_inner]  states at block starts
 //   part_bc [tiles][batch][seqlen][2*d_state]          per-tile dB | dC sums
 //   part_a  [c][batch][d_inner][d_state]               per-(chunk, row) dA
@@ -149,7 +155,7 @@ struct BwdWorkspace {
   float* lIn;
 };
 BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                                  const BwdPlan& plan, int64_t* total_floats);
+                                  const BwdPlan& plan, bool ckpt_given, int64_t* total_floats);
 hipError_t launch_scan_bwd(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPlan& pl);
 
 // Scan with a scalar decay per head (Mamba-2 / SSD form).  bf16 io (x, dt,

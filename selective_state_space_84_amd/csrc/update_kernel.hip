@@ -147,7 +147,7 @@ __global__ void __launch_bounds__(kUpdBlock)
     const int64_t b = b0 + r * rows;
     const float xv = xr[r];
     float dv = dr[r];
-    if (MODE & 1) dv = softplus(dv + dtb);
+    if (MODE & 1) dv = softplus(dv, dtb);
     const float wx = dv * xv;
     float acc = 0.f;
 #pragma unroll

@@ -21,6 +21,14 @@ Recipe (the same for every consumer):
     log(1..N), A = -exp(A_log); "Mamba from principle to code"
     (lshu.cn/news/79586) section 6.2, derivation page section 5.1).
   * D[d] = 1 (derivation page section 5.1).
+  * ``params="random"`` instead draws the per-channel parameters a trained
+    layer would hold (A_log and D are learnable per channel, derivation page
+    section 5.1): A[d, n] = -exp(N(0, 1)) clipped to [-20, -0.05], independent
+    per (d, n), and D[d] ~ N(0, 1), from their own stream
+    ``SeedSequence([seed, 0xA11]).spawn(2)`` = [A, D], so the other tensors
+    are the same as with the default ``params="s4d"``.  The parity tests use
+    it so that every per-channel index of A and D is checked; the layer
+    configs keep the S4D-real initialisation.
   * h0 ~ N(0, 0.1^2) per state when a nonzero initial state is asked for.
   * Values are drawn and computed in float64, rounded to float32 (nearest
     even), and for bf16 tensors rounded again to bfloat16 (nearest even).
@@ -123,6 +131,26 @@ def _inv_softplus(u: np.ndarray) -> np.ndarray:
     return np.log(np.expm1(u))
 
 
+def _channel_params(d_inner: int, d_state: int, seed: int, params: str):
+    """(A, D) fp32: the S4D-real initialisation, or random per-channel values."""
+    if params == "s4d":
+        A = np.ascontiguousarray(
+            np.broadcast_to(-(np.arange(1, d_state + 1, dtype=np.float64)), (d_inner, d_state))).astype(np.float32)
+        return A, np.ones(d_inner, dtype=np.float32)
+    ka, kd = np.random.SeedSequence([seed, 0xA11]).spawn(2)
+    if params == "random":
+        scale = np.exp(np.random.default_rng(ka).uniform(-0.5, 0.5, (d_inner, d_state)))
+        A = round_to_f32(-(np.arange(1, d_state + 1, dtype=np.float64))[None, :] * scale)
+        D = round_to_f32(1.0 + 0.5 * np.random.default_rng(kd).standard_normal(d_inner))
+        return A, D
+    if params == "wide":
+        a = np.exp(np.random.default_rng(ka).standard_normal((d_inner, d_state)))
+        A = round_to_f32(-np.clip(a, 0.05, 20.0))
+        D = round_to_f32(np.random.default_rng(kd).standard_normal(d_inner))
+        return A, D
+    raise ValueError("params must be 's4d', 'random' or 'wide', got %r" % (params,))
+
+
 def _threads(threads: Optional[int]) -> int:
     if threads:
         return threads
@@ -135,7 +163,7 @@ def _threads(threads: Optional[int]) -> int:
 
 def make_scan_inputs(batch: int, seqlen: int, d_inner: int, d_state: int, dtype: str, seed: int,
                      nonzero_h0: bool = False, threads: Optional[int] = None,
-                     raw_delta: bool = False) -> Dict[str, np.ndarray]:
+                     raw_delta: bool = False, params: str = "s4d") -> Dict[str, np.ndarray]:
     """Host tensors for one scan call.
 
     Returns x, delta, z (batch, seqlen, d_inner), B, C (batch, seqlen, d_state)
@@ -180,9 +208,7 @@ def make_scan_inputs(batch: int, seqlen: int, d_inner: int, d_state: int, dtype:
     else:
         for t in range(tasks):
             fill(t)
-    out["A"] = np.ascontiguousarray(
-        np.broadcast_to(-(np.arange(1, d_state + 1, dtype=np.float64)), (d_inner, d_state))).astype(np.float32)
-    out["D"] = np.ones(d_inner, dtype=np.float32)
+    out["A"], out["D"] = _channel_params(d_inner, d_state, seed, params)
     out["dt_bias"] = round_to_f32(inv_sp) if raw_delta else round_to_f32(u)
     if nonzero_h0:
         out["h0"] = round_to_f32(0.1 * np.random.default_rng(kids["h0"]).standard_normal((batch, d_inner, d_state)))
@@ -197,7 +223,8 @@ def scan_inputs(cfg: ScanConfig, threads: Optional[int] = None) -> Dict[str, np.
 
 
 def make_decode_inputs(batch: int, d_inner: int, d_state: int, dtype: str, steps: int, seed: int,
-                       threads: Optional[int] = None, raw_delta: bool = False) -> Dict[str, np.ndarray]:
+                       threads: Optional[int] = None, raw_delta: bool = False,
+                       params: str = "s4d") -> Dict[str, np.ndarray]:
     """Host tensors for ``steps`` consecutive decode steps.
 
     x, delta, z: (steps, batch, d_inner); B, C: (steps, batch, d_state) in the
@@ -230,9 +257,7 @@ def make_decode_inputs(batch: int, d_inner: int, d_state: int, dtype: str, steps
     else:
         for s in range(steps):
             fill(s)
-    out["A"] = np.ascontiguousarray(
-        np.broadcast_to(-(np.arange(1, d_state + 1, dtype=np.float64)), (d_inner, d_state))).astype(np.float32)
-    out["D"] = np.ones(d_inner, dtype=np.float32)
+    out["A"], out["D"] = _channel_params(d_inner, d_state, seed, params)
     out["dt_bias"] = round_to_f32(inv_sp) if raw_delta else round_to_f32(u)
     return out
 
@@ -268,7 +293,7 @@ def make_scan_grads(batch: int, seqlen: int, d_inner: int, d_state: int, dtype: 
 
 def make_ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, ngroups: int, d_state: int, seed: int,
                     nonzero_h0: bool = False, raw_dt: bool = False,
-                    threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+                    threads: Optional[int] = None, params: str = "s4d") -> Dict[str, np.ndarray]:
     """Host tensors for the scan with a scalar decay per head (bf16 io).
 
     x, z: (batch, seqlen, nheads, headdim) ~ N(0,1); dt: (batch, seqlen,
@@ -276,6 +301,9 @@ def make_ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, ngroups:
     ``raw_dt`` the raw 0.5*N(0,1) and dt_bias = inv_softplus(U)); B, C:
     (batch, seqlen, ngroups, d_state) ~ N(0,1); A_h = -U[1, 16]; D = 1; h0 ~
     N(0, 0.1^2) if requested.  Per-row streams, like the other generators.
+    ``params="random"`` draws D_h ~ N(0, 1) per head instead (its own stream,
+    ``SeedSequence([seed, 0xA11, 1])``), so a head-indexing mistake in the
+    skip term shows.
     """
     kids = np.random.SeedSequence([seed, 0x55D]).spawn(8)
     r = np.random.default_rng(kids[0])
@@ -304,7 +332,12 @@ def make_ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, ngroups:
         for b in range(batch):
             fill(b)
     out["A"] = round_to_f32(A)
-    out["D"] = np.ones(nheads, dtype=np.float32)
+    if params == "random":
+        out["D"] = round_to_f32(np.random.default_rng(np.random.SeedSequence([seed, 0xA11, 1])).standard_normal(nheads))
+    elif params == "s4d":
+        out["D"] = np.ones(nheads, dtype=np.float32)
+    else:
+        raise ValueError("params must be 's4d' or 'random', got %r" % (params,))
     out["dt_bias"] = round_to_f32(inv_sp) if raw_dt else round_to_f32(u)
     out["h0"] = (round_to_f32(0.1 * np.random.default_rng(kids[7]).standard_normal((batch, nheads, headdim, d_state)))
                  if nonzero_h0 else None)

@@ -193,6 +193,21 @@ def test_bwd_workspace_size(lib):
     assert lib.ssm_scan_bwd_workspace_size(b, L, d, 32) == ctypes.c_size_t(-1).value
     assert lib.ssm_scan_bwd_workspace_size(-1, L, d, N) == ctypes.c_size_t(-1).value
     assert bd.scan_bwd_workspace_size(0, 0, 0, 16) == 0
+    # With the forward call's checkpoints the checkpoint section is left out.
+    assert lib.ssm_scan_bwd_workspace_size_ex(b, L, d, N, 0) == want
+    assert lib.ssm_scan_bwd_workspace_size_ex(b, L, d, N, 1) == want - up(b * nblk * N * d) * 4
+    assert lib.ssm_scan_bwd_workspace_size_ex(b, L, d, N, 2) == ctypes.c_size_t(-1).value
+    # A chunked plan (few channels, long sequence) also drops the forward chunk
+    # summaries and entry states, which only serve to compute checkpoints.
+    b, L, d = 2, 1013, 70
+    tiles, nblk, S = 2, 127, 2 * 70 * 16
+    cb = -(-nblk // min(-(-16384 // (b * tiles)), L // 64))
+    nch = -(-nblk // cb)
+    assert nch > 1
+    sums = 2 * up((nch - 1) * S) + up(nch * S)  # P, S, entry states: forward and adjoint sets alike
+    full = (up(b * nblk * N * d) + up(tiles * b * L * 2 * N) + up(nch * S) + 2 * up(nch * b * d) + 2 * sums) * 4
+    assert lib.ssm_scan_bwd_workspace_size(b, L, d, N) == full
+    assert lib.ssm_scan_bwd_workspace_size_ex(b, L, d, N, 1) == full - (up(b * nblk * N * d) + sums) * 4
 
 
 def test_bwd_argument_errors(lib):
@@ -235,6 +250,9 @@ def test_bwd_argument_errors(lib):
     need = lib.ssm_scan_bwd_workspace_size(2, 4, 8, 16)
     assert _bwd(lib, ws_bytes=need - 4) == bd.SSM_ERR_WORKSPACE
     assert _bwd(lib, ws=P0 + 64 * MB + 16) == bd.SSM_ERR_MISALIGNED
+    need_ck = lib.ssm_scan_bwd_workspace_size_ex(2, 4, 8, 16, 1)
+    assert 0 < need_ck < need
+    assert _bwd(lib, ckpt=P0 + 40 * MB, ws_bytes=need_ck - 4) == bd.SSM_ERR_WORKSPACE
 
 
 def _ssd(lib, x=P0, dt=P0 + MB, A=P0 + 2 * MB, B=P0 + 3 * MB, C=P0 + 4 * MB, D=None, z=None, h0=None,

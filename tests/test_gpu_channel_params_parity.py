@@ -1,0 +1,212 @@
+"""GPU parity with per-channel parameters: A[d, n] and D[d] differ from
+channel to channel (and from state to state), as in a trained layer (A_log
+and D are learnable per channel: "Deriving and implementing Mamba from
+scratch" (dpshk.com/news/3333417) section 5.1).  With the S4D-real
+initialisation every channel holds the same A row and D = 1, so a kernel that
+read channel 0's parameters for every channel would still match the oracle;
+these cases would not (tests/test_channel_params_inputs.py checks on the CPU
+that such a mistake moves the result far beyond every gate).
+
+Families covered: the scan (every state split, sequence chunks, every
+d_state, every step mode), the decode update (every d_state, every step
+mode), the backward pass (every step mode, sequence chunks, from forward
+checkpoints) and the SSD form (per-head D).  "random" parameters are
+A[d, n] = -(n+1) exp(U[-0.5, 0.5]), D ~ N(1, 0.5); "wide" ones are
+A = -exp(N(0, 1)) clipped to [0.05, 20], D ~ N(0, 1), run at the bf16 gate.
+fp32 cases are gated at 1e-5, raised only where fp32 arithmetic itself
+exceeds it on that very case (f32_gate in test_tolerance_floor.py: 1.5x the
+case's emulated fp32 floor).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from conftest import floored_rel_err
+from selective_state_space_84_amd import inputs
+from test_tolerance_bwd import BWD_F32_GATE
+from test_tolerance_floor import decode_f32_gate, f32_gate
+
+pytestmark = pytest.mark.gpu
+
+SP = 0x1
+ZOH = 0x2
+BF16_GATE = 2e-2
+
+
+def _scan_check(inp, dtype, flags=0, label="", **opts):
+    import torch
+    from gpu_util import dev_inputs, to_dev, to_host_f64
+    from selective_state_space_84_amd import binding
+    print("case", label, inp["x"].shape, dtype, flags, opts, flush=True)
+    d = dev_inputs(inp)
+    dtb = to_dev(inp["dt_bias"]) if flags & SP else None
+    y, hl = binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], flags=flags,
+                                 dt_bias=dtb, **opts)
+    torch.cuda.synchronize()
+    ry, rh = oracle.scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
+                         inp["dt_bias"] if flags & SP else None, exact_zoh=bool(flags & ZOH),
+                         delta_softplus=bool(flags & SP))
+    ey, eh = floored_rel_err(to_host_f64(y), ry), floored_rel_err(to_host_f64(hl), rh)
+    tol = f32_gate(inp, flags) if dtype == "f32" else BF16_GATE
+    print("  errors y %.2e h %.2e gate %.1e" % (ey, eh, tol), flush=True)
+    assert ey <= tol and eh <= tol, (ey, eh, tol)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_split", [1, 2, 4, 8])
+def test_scan_every_split(lib, dtype, n_split):
+    inp = inputs.make_scan_inputs(3, 100, 200, 16, dtype, 3100 + n_split, nonzero_h0=True, params="random")
+    _scan_check(inp, dtype, n_split=n_split, label="split%d" % n_split)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk_len,n_split", [(7, 1), (24, 4), (64, 1), (13, 2)])
+def test_scan_sequence_chunks(lib, dtype, chunk_len, n_split):
+    inp = inputs.make_scan_inputs(2, 150, 130, 16, dtype, 3200 + chunk_len, nonzero_h0=True, params="random")
+    _scan_check(inp, dtype, n_split=n_split, chunk_len=chunk_len, label="chunk%d" % chunk_len)
+
+
+@pytest.mark.parametrize("d_state", [2, 4, 8, 32, 64, 128])
+def test_scan_d_state(lib, d_state):
+    inp = inputs.make_scan_inputs(2, 40, 70, d_state, "f32", 3300 + d_state, nonzero_h0=True, params="random")
+    _scan_check(inp, "f32", label="N%d" % d_state)
+
+
+@pytest.mark.parametrize("flags", [SP, ZOH, SP | ZOH])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_split,chunk_len", [(1, 0), (4, 0), (1, 16)])
+def test_scan_step_modes(lib, flags, dtype, n_split, chunk_len):
+    inp = inputs.make_scan_inputs(3, 100, 200, 16, dtype, 3400 + 10 * flags + n_split + chunk_len, nonzero_h0=True,
+                                  raw_delta=bool(flags & SP), params="random")
+    _scan_check(inp, dtype, flags, n_split=n_split, chunk_len=chunk_len, label="mode%d" % flags)
+
+
+@pytest.mark.parametrize("chunk_len", [0, 32])
+def test_scan_wide_parameters_bf16(lib, chunk_len):
+    inp = inputs.make_scan_inputs(2, 300, 200, 16, "bf16", 3500 + chunk_len, nonzero_h0=True, params="wide")
+    _scan_check(inp, "bf16", chunk_len=chunk_len, label="wide")
+
+
+def test_scan_long_sequence_fp32(lib):
+    """1000 steps in fp32 with per-channel parameters (slow channels keep a
+    long memory)."""
+    inp = inputs.make_scan_inputs(1, 1000, 96, 16, "f32", 3600, nonzero_h0=True, params="random")
+    _scan_check(inp, "f32", label="L1000")
+
+
+def _decode_run(inp, steps, flags):
+    import torch
+    from gpu_util import to_dev, to_host_f64
+    from selective_state_space_84_amd import binding
+    batch, d_inner = inp["x"].shape[1:]
+    d_state = inp["A"].shape[1]
+    A, D = to_dev(inp["A"]), to_dev(inp["D"])
+    dtb = to_dev(inp["dt_bias"]) if flags & SP else None
+    h = torch.zeros((batch, d_inner, d_state), dtype=torch.float32, device="cuda:0")
+    X, DL, Z, Bm, Cm = (to_dev(inp[k][:steps]) for k in ("x", "delta", "z", "B", "C"))
+    Y = torch.empty_like(X)
+    for s in range(steps):
+        binding.ssm_state_update(h, X[s], DL[s], A, Bm[s], Cm[s], D, Z[s], y_t=Y[s], flags=flags, dt_bias=dtb)
+    torch.cuda.synchronize()
+    return to_host_f64(Y), to_host_f64(h)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d_state", [2, 4, 8, 16, 32, 64])
+@pytest.mark.parametrize("flags", [0, SP | ZOH])
+def test_decode_every_d_state(lib, dtype, d_state, flags):
+    steps = 12
+    inp = inputs.make_decode_inputs(5, 300, d_state, dtype, steps, 3700 + d_state + flags, raw_delta=bool(flags & SP),
+                                    params="random")
+    print("case decode", dtype, d_state, flags, flush=True)
+    Y, h = _decode_run(inp, steps, flags)
+    hr = np.zeros((5, 300, d_state))
+    tol = decode_f32_gate(inp, steps, flags) if dtype == "f32" else BF16_GATE
+    for s in range(steps):
+        yr, hr = oracle.update(hr, inp["x"][s], inp["delta"][s], inp["A"], inp["B"][s], inp["C"][s], inp["D"],
+                               inp["z"][s], inp["dt_bias"] if flags & SP else None, exact_zoh=bool(flags & ZOH),
+                               delta_softplus=bool(flags & SP))
+        assert floored_rel_err(Y[s], yr) <= tol, "step %d" % s
+    assert floored_rel_err(h, hr) <= tol
+
+
+def _bwd_gpu(inp, gr, flags, ckpt=None):
+    import torch
+    from gpu_util import to_dev, to_host_f64
+    from selective_state_space_84_amd import binding
+    d = {k: to_dev(inp.get(k)) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "dt_bias")}
+    g = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], dy=to_dev(gr["dy"]),
+                             dh_last=to_dev(gr["dh_last"]), flags=flags,
+                             dt_bias=d["dt_bias"] if flags & SP else None, ckpt=ckpt)
+    torch.cuda.synchronize()
+    return {k: to_host_f64(v) for k, v in g.items()}
+
+
+def _bwd_ref(inp, gr, flags):
+    return oracle.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
+                           inp["dt_bias"] if flags & SP else None, dy=gr["dy"], dh_last=gr["dh_last"],
+                           delta_softplus=bool(flags & SP), exact_zoh=bool(flags & ZOH))
+
+
+def _bwd_compare(g, r, gate, label):
+    errs = {k: floored_rel_err(g[k], r[k]) for k in r if k in g and r[k].size}
+    print(label, " ".join("%s %.2e" % kv for kv in errs.items()), flush=True)
+    for k, e in errs.items():
+        assert e <= gate, (k, e)
+
+
+@pytest.mark.parametrize("flags", [0, SP, ZOH, SP | ZOH])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_every_mode(lib, flags, dtype):
+    inp = inputs.make_scan_inputs(2, 45, 130, 16, dtype, 3800 + flags, nonzero_h0=True, raw_delta=bool(flags & SP),
+                                  params="random")
+    gr = inputs.make_scan_grads(2, 45, 130, 16, dtype, 3800 + flags)
+    print("case bwd", flags, dtype, flush=True)
+    _bwd_compare(_bwd_gpu(inp, gr, flags), _bwd_ref(inp, gr, flags), BWD_F32_GATE if dtype == "f32" else BF16_GATE,
+                 "bwd mode %d %s" % (flags, dtype))
+
+
+@pytest.mark.parametrize("d_state", [2, 4, 8])
+def test_bwd_small_d_state(lib, d_state):
+    inp = inputs.make_scan_inputs(2, 37, 100, d_state, "f32", 3850 + d_state, nonzero_h0=True, params="random")
+    gr = inputs.make_scan_grads(2, 37, 100, d_state, "f32", 3850 + d_state)
+    _bwd_compare(_bwd_gpu(inp, gr, 0), _bwd_ref(inp, gr, 0), BWD_F32_GATE, "bwd N=%d" % d_state)
+
+
+@pytest.mark.parametrize("flags", [0, SP | ZOH])
+@pytest.mark.parametrize("fwd_ckpt", [False, True])
+def test_bwd_sequence_chunks_and_checkpoints(lib, flags, fwd_ckpt):
+    """A long sequence with few channels (the backward cuts it into chunks),
+    standalone or fed with the forward call's checkpoints."""
+    import torch
+    from gpu_util import to_dev
+    from selective_state_space_84_amd import binding
+    batch, L, dI, N = 2, 1013, 70, 16
+    inp = inputs.make_scan_inputs(batch, L, dI, N, "f32", 3900 + flags + fwd_ckpt, nonzero_h0=True,
+                                  raw_delta=bool(flags & SP), params="random")
+    gr = inputs.make_scan_grads(batch, L, dI, N, "f32", 3900 + flags)
+    print("case bwd chunks", flags, fwd_ckpt, flush=True)
+    ck = None
+    if fwd_ckpt:
+        d = {k: to_dev(inp.get(k)) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "dt_bias")}
+        ck = torch.empty((binding.scan_ckpt_bytes(batch, L, dI, N) // 4,), device="cuda:0")
+        binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], ckpt_out=ck,
+                             flags=flags, dt_bias=d["dt_bias"] if flags & SP else None)
+    _bwd_compare(_bwd_gpu(inp, gr, flags, ckpt=ck), _bwd_ref(inp, gr, flags), BWD_F32_GATE,
+                 "bwd chunks mode %d ckpt %d" % (flags, fwd_ckpt))
+
+
+@pytest.mark.parametrize("d_state,ngroups", [(64, 1), (128, 2)])
+def test_ssd_per_head_skip(lib, d_state, ngroups):
+    import torch
+    from gpu_util import to_dev, to_host_f64
+    from selective_state_space_84_amd import binding
+    inp = inputs.make_ssd_inputs(2, 150, 4, 64, ngroups, d_state, 3950 + d_state, nonzero_h0=True, params="random")
+    d = {k: to_dev(inp.get(k)) for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")}
+    y, hl = binding.ssm_ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"])
+    torch.cuda.synchronize()
+    ry, rh = oracle.ssd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"])
+    ey, eh = floored_rel_err(to_host_f64(y), ry), floored_rel_err(to_host_f64(hl), rh)
+    print("ssd random D", d_state, ngroups, "y %.2e h %.2e" % (ey, eh), flush=True)
+    assert ey <= BF16_GATE and eh <= BF16_GATE
+

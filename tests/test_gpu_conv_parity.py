@@ -26,7 +26,7 @@ def _run(inp, silu, use_state, use_bias=True):
 @pytest.mark.parametrize("K", [2, 3, 4])
 @pytest.mark.parametrize("silu,use_state", [(True, True), (False, False), (True, False)])
 def test_conv_ragged(lib, dtype, K, silu, use_state):
-    # 70 steps: ragged against the 32-step thread segment; 200 channels: ragged against the tile.
+    # 70 steps: one full 64-step thread segment and a ragged one; 200 channels: ragged against the tile.
     inp = inputs.make_conv_inputs(3, 70, 200, K, dtype, 1100 + K, with_state=use_state)
     print("case conv", dtype, K, silu, use_state, flush=True)
     y, so = _run(inp, silu, use_state)

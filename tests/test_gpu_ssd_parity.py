@@ -43,7 +43,7 @@ def _check(got, ref, label):
 @pytest.mark.parametrize("d_state", [64, 128])
 @pytest.mark.parametrize("ngroups", [1, 2])
 def test_ssd_ragged_all_options(lib, d_state, ngroups):
-    """150 steps: two full 64-step chunks and a ragged one; every option."""
+    """150 steps: four full 32-step chunks and a ragged one; every option."""
     inp = inputs.make_ssd_inputs(2, 150, 4, 64, ngroups, d_state, 2000 + d_state + ngroups, nonzero_h0=True)
     print("case ssd", d_state, ngroups, flush=True)
     _check(_gpu(inp), _ref(inp), "ssd N=%d G=%d" % (d_state, ngroups))

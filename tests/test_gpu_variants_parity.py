@@ -5,9 +5,11 @@ softplus(delta + dt_bias[d]) (selection step, "Deriving and implementing
 Mamba from scratch" section 4.1).  Exact ZOH: the input term is
 (exp(delta a) - 1) / a * B (same page, section 2.2), with the a = 0 limit
 delta * B.  Same metric as the plain scan; gates 2e-2 for bf16 io and, for
-fp32 io, the variant gate sized in test_tolerance_floor.py (a correctly
-rounded fp32 implementation of the softplus step already exceeds 1e-5 on
-some shapes).
+fp32 io, the benchmark spec's 1e-5, raised only where fp32 arithmetic itself
+exceeds it on that very case (f32_gate / decode_f32_gate in
+test_tolerance_floor.py: 1.5x the case's emulated fp32 floor; it happens for
+the exact ZOH and for the softplus step at d_state 128).  Every family also runs on
+random per-channel A and D (inputs.make_scan_inputs(params="random")).
 """
 import numpy as np
 import pytest
@@ -15,7 +17,7 @@ import pytest
 import oracle
 from conftest import floored_rel_err
 from selective_state_space_84_amd import binding, inputs
-from test_tolerance_floor import VARIANT_F32_GATE
+from test_tolerance_floor import decode_f32_gate, f32_gate
 
 pytestmark = pytest.mark.gpu
 
@@ -23,8 +25,9 @@ SP = binding.SSM_FLAG_DELTA_SOFTPLUS
 ZOH = binding.SSM_FLAG_EXACT_ZOH
 
 
-def _gen(batch, L, d, N, dtype, seed, flags, h0=True, zero_a=False):
-    inp = inputs.make_scan_inputs(batch, L, d, N, dtype, seed, nonzero_h0=h0, raw_delta=bool(flags & SP))
+def _gen(batch, L, d, N, dtype, seed, flags, h0=True, zero_a=False, params="s4d"):
+    inp = inputs.make_scan_inputs(batch, L, d, N, dtype, seed, nonzero_h0=h0, raw_delta=bool(flags & SP),
+                                  params=params)
     if zero_a:
         # a few a = 0 entries exercise the limit delta * B of the exact ZOH
         inp["A"][::7, 0] = 0.0
@@ -48,17 +51,19 @@ def _check(inp, dtype, flags, **opts):
                                  dt_bias=dtb, **opts)
     torch.cuda.synchronize()
     ry, rh = _oracle(inp, flags)
-    tol = VARIANT_F32_GATE if dtype == "f32" else 2e-2
+    tol = f32_gate(inp, flags) if dtype == "f32" else 2e-2
     ey, eh = floored_rel_err(to_host_f64(y), ry), floored_rel_err(to_host_f64(hl), rh)
+    print("errors y %.2e h %.2e gate %.1e" % (ey, eh, tol), flush=True)
     assert ey <= tol and eh <= tol, (ey, eh, tol)
     return ey, eh
 
 
+@pytest.mark.parametrize("params", ["s4d", "random"])
 @pytest.mark.parametrize("flags", [SP, ZOH, SP | ZOH])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("n_split,chunk_len", [(1, 0), (2, 0), (8, 0), (1, 24), (4, 13)])
-def test_scan_variants(lib, flags, dtype, n_split, chunk_len):
-    inp = _gen(3, 100, 200, 16, dtype, 900 + flags * 10 + n_split, flags)
+def test_scan_variants(lib, flags, dtype, n_split, chunk_len, params):
+    inp = _gen(3, 100, 200, 16, dtype, 900 + flags * 10 + n_split, flags, params=params)
     _check(inp, dtype, flags, n_split=n_split, chunk_len=chunk_len)
 
 
@@ -72,10 +77,11 @@ def test_exact_zoh_zero_a_limit(lib, flags, dtype):
     _check(inp, dtype, flags, n_split=2)
 
 
+@pytest.mark.parametrize("params", ["s4d", "random"])
 @pytest.mark.parametrize("flags", [SP, ZOH, SP | ZOH])
 @pytest.mark.parametrize("d_state", [2, 8, 64, 128])
-def test_scan_variants_d_state(lib, flags, d_state):
-    inp = _gen(2, 40, 70, d_state, "f32", 950 + d_state, flags)
+def test_scan_variants_d_state(lib, flags, d_state, params):
+    inp = _gen(2, 40, 70, d_state, "f32", 950 + d_state, flags, params=params)
     _check(inp, "f32", flags)
 
 
@@ -104,21 +110,23 @@ def test_scan_variants_full_size_sampled(lib, flags):
     assert ey <= 2e-2 and eh <= 2e-2
 
 
+@pytest.mark.parametrize("params", ["s4d", "random"])
 @pytest.mark.parametrize("flags", [SP, ZOH, SP | ZOH])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d_state", [4, 16, 64])
-def test_update_variants(lib, flags, dtype, d_state):
+def test_update_variants(lib, flags, dtype, d_state, params):
     import torch
     from gpu_util import to_dev, to_host_f64
     steps = 8
-    inp = inputs.make_decode_inputs(4, 300, d_state, dtype, steps, 970 + flags + d_state, raw_delta=bool(flags & SP))
+    inp = inputs.make_decode_inputs(4, 300, d_state, dtype, steps, 970 + flags + d_state, raw_delta=bool(flags & SP),
+                                    params=params)
     if flags & ZOH:
         inp["A"][::5, 1] = 0.0
     A, D = to_dev(inp["A"]), to_dev(inp["D"])
     dtb = to_dev(inp["dt_bias"]) if flags & SP else None
     h = torch.zeros((4, 300, d_state), dtype=torch.float32, device="cuda:0")
     hr = np.zeros((4, 300, d_state))
-    tol = VARIANT_F32_GATE if dtype == "f32" else 2e-2
+    tol = decode_f32_gate(inp, steps, flags) if dtype == "f32" else 2e-2
     for s in range(steps):
         xs = {k: to_dev(np.ascontiguousarray(inp[k][s])) for k in ("x", "delta", "z", "B", "C")}
         yt = binding.ssm_state_update(h, xs["x"], xs["delta"], A, xs["B"], xs["C"], D, xs["z"], flags=flags,
