@@ -40,7 +40,8 @@
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
  *     library never frees, keeps or allocates them.  It allocates nothing on
- *     any path and holds no mutable global state; concurrent calls on
+ *     any path and holds no mutable global state, except the per-device
+ *     scratch of ssm_scan_fwd_noalloc (see there); concurrent calls on
  *     different streams with disjoint outputs are safe.
  *   - Tensors are dense, row-major (C order), with the shapes given below.
  *   - io_dtype selects the element type of x, delta, z, B, C and y:
@@ -187,6 +188,36 @@ int ssm_scan_fwd_ex(const void* x, const void* delta, const float* A, const void
                     const void* z, const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen,
                     int64_t d_inner, int64_t d_state, int32_t io_dtype, const ssm_scan_opts_t* opts,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssm_scan_fwd_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It allocates nothing: when the
+ * sequence is split into chunks, the chunk carries live in a device scratch
+ * array of ssm_scan_fwd_noalloc_max_bytes() bytes (64 MiB) that the library
+ * holds on each device it runs on, from the first call on that device until
+ * the process ends.
+ *   - Arguments, results and errors as for ssm_scan_fwd_ex (opts may be NULL).
+ *   - With an automatic chunk length (opts NULL or chunk_len 0) the plan keeps
+ *     as many chunks as the scratch holds ((3 n - 2) * batch * d_inner *
+ *     d_state floats for n chunks), down to one unsplit sweep; results equal
+ *     ssm_scan_fwd_ex's up to fp32 rounding of the chunk carries.
+ *   - An explicit chunk_len whose carries exceed the scratch returns
+ *     SSM_ERR_WORKSPACE before anything is enqueued.
+ *   - The scratch keeps the last call's contents (nothing in it needs to start
+ *     at zero).  Every call on one device shares that device's scratch: calls
+ *     that overlap in time on one device (different streams or threads) race
+ *     and must be serialised by the caller.
+ *   - Its first call on a device looks up the scratch's device address
+ *     (SSM_ERR_HIP if that fails).
+ */
+int ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                         const float* D, const void* z, const float* h0, void* y, float* h_last, int64_t batch,
+                         int64_t seqlen, int64_t d_inner, int64_t d_state, int32_t io_dtype,
+                         const ssm_scan_opts_t* opts, void* stream);
+
+/* Size of the per-device scratch ssm_scan_fwd_noalloc uses (64 MiB). */
+size_t ssm_scan_fwd_noalloc_max_bytes(void);
 
 /*
  * Single-token recurrent update (decode), in place on h.

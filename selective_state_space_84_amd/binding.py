@@ -53,6 +53,8 @@ SIGNATURES = {
                            ctypes.POINTER(_I64), ctypes.POINTER(_I64)], ctypes.c_int),
     "ssm_scan_fwd": ([_P] * 10 + [_I64] * 4 + [_I32, _P, _SZ, _P], ctypes.c_int),
     "ssm_scan_fwd_ex": ([_P] * 10 + [_I64] * 4 + [_I32, ctypes.POINTER(ScanOpts), _P, _SZ, _P], ctypes.c_int),
+    "ssm_scan_fwd_noalloc": ([_P] * 10 + [_I64] * 4 + [_I32, ctypes.POINTER(ScanOpts), _P], ctypes.c_int),
+    "ssm_scan_fwd_noalloc_max_bytes": ([], _SZ),
     "ssm_state_update": ([_P] * 9 + [_I64] * 3 + [_I32, _P], ctypes.c_int),
     "ssm_state_update_ex": ([_P] * 9 + [_I64] * 3 + [_I32, _U32, _P, _P], ctypes.c_int),
     "ssm_scan_bwd_workspace_size": ([_I64, _I64, _I64, _I64], _SZ),
@@ -190,6 +192,21 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, y=None, h_last=N
         batch, seqlen, d_inner, d_state, dt, ctypes.byref(o), _ptr(workspace), ws_have, _stream(stream))
     if rc != SSM_OK:
         raise SsmError(rc, "ssm_scan_fwd")
+    return y, h_last
+
+
+def ssm_scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, h0=None, *, y, h_last=None, n_split=0, chunk_len=0,
+                         flags=0, dt_bias=None, stream=None):
+    """ssm_scan_fwd without a workspace: the library's per-device scratch holds
+    the chunk carries and nothing is allocated (y and h_last must be given)."""
+    batch, seqlen, d_inner = x.shape
+    d_state = A.shape[1]
+    o = _opts(n_split, chunk_len, flags, dt_bias, None)
+    rc = load_library().ssm_scan_fwd_noalloc(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
+        batch, seqlen, d_inner, d_state, _io_dtype(x), ctypes.byref(o), _stream(stream))
+    if rc != SSM_OK:
+        raise SsmError(rc, "ssm_scan_fwd_noalloc")
     return y, h_last
 
 

@@ -8,6 +8,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace ssm {
 int64_t update_grid_blocks(int64_t batch, int64_t d_inner, int32_t d_state);
 }
@@ -131,10 +133,59 @@ int workspace_bytes_for(int64_t batch, int64_t d_inner, int64_t d_state, const P
   return SSM_OK;
 }
 
+// Device scratch of ssm_scan_fwd_noalloc: the chunk carries (decay products,
+// zero-start end states, entry states) of a split sequence live here instead
+// of in a caller workspace.  Each device holds its own copy from the first
+// call on it until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is taken once per device
+// with hipGetSymbolAddress (with that device current) and only that address is
+// handed to kernels.  Calls that overlap on one device share it and race.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+
+// The current device's scratch address (SSM_OK), or SSM_ERR_HIP.
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return SSM_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return SSM_ERR_HIP;
+  *out = g_scratch_ptr[dev];
+  return SSM_OK;
+}
+
+// With no caller workspace, the automatic plan keeps as many sequence chunks
+// as the scratch holds: n chunks need (3n - 2) * batch * d_inner * d_state
+// floats.  Fewer than two fitting chunks means one unsplit sweep.
+void cap_plan_to_scratch(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, Plan* pl) {
+  const int64_t states = batch * d_inner * d_state;
+  if (pl->n_chunks <= 1 || states <= 0) return;
+  const int64_t n_max = ((int64_t)(kScratchBytes / sizeof(float)) / states + 2) / 3;
+  if (pl->n_chunks <= n_max) return;
+  if (n_max < 2) {
+    pl->chunk_len = seqlen;
+    pl->n_chunks = 1;
+    return;
+  }
+  int64_t cl = (seqlen + n_max - 1) / n_max;
+  cl = (cl + ssm::kTimeBlock - 1) / ssm::kTimeBlock * ssm::kTimeBlock;
+  if (cl > seqlen) cl = seqlen;
+  pl->chunk_len = cl;
+  pl->n_chunks = (seqlen + cl - 1) / cl;
+}
+
 int scan_impl(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
               const void* z, const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen,
               int64_t d_inner, int64_t d_state, int32_t io_dtype, const ssm_scan_opts_t* opts, void* workspace,
-              size_t workspace_bytes, void* stream) {
+              size_t workspace_bytes, void* stream, bool use_scratch = false) {
   int rc = check_dims(batch, seqlen, d_inner, d_state);
   if (rc != SSM_OK) return rc;
   if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
@@ -202,13 +253,18 @@ int scan_impl(const void* x, const void* delta, const float* A, const void* B, c
   Plan pl;
   rc = make_plan(batch, seqlen, d_inner, d_state, opts, &pl);
   if (rc != SSM_OK) return rc;
+  const bool auto_chunks = opts == nullptr || opts->chunk_len == 0;
+  if (use_scratch && auto_chunks) cap_plan_to_scratch(batch, seqlen, d_inner, d_state, &pl);
   size_t need;
   rc = workspace_bytes_for(batch, d_inner, d_state, pl, &need);
   if (rc != SSM_OK) return rc;
   const int64_t tiles = (d_inner + 63) / 64;
   int64_t grid;
   if (!mul3(batch, pl.n_chunks, tiles, &grid) || grid > INT32_MAX) return SSM_ERR_BAD_DIM;
-  if (need > 0) {
+  if (use_scratch) {
+    // An explicit chunk length whose carries do not fit the scratch.
+    if (need > kScratchBytes) return SSM_ERR_WORKSPACE;
+  } else if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return SSM_ERR_WORKSPACE;
     if (!aligned(workspace, kWorkspaceAlign)) return SSM_ERR_MISALIGNED;
     const void* all[] = {x, delta, z, B, C, A, D, h0, y, h_last, dt_bias};
@@ -226,6 +282,13 @@ int scan_impl(const void* x, const void* delta, const float* A, const void* B, c
   if (seqlen == 0) {
     if (h_last == nullptr || h_last == h0) return SSM_OK;
     return ssm::launch_state_fill(h_last, h0, n_h, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
+  if (use_scratch) {
+    workspace = nullptr;
+    if (need > 0) {
+      rc = device_scratch(&workspace);
+      if (rc != SSM_OK) return rc;
+    }
   }
   ssm::ScanLaunch p{x, delta, A, B, C, D, z, h0, y, h_last, static_cast<float*>(workspace), ckpt, dt_bias, flags, batch,
                     seqlen, d_inner, (int32_t)d_state, pl.n_split, pl.chunk_len, pl.n_chunks,
@@ -587,6 +650,16 @@ int ssm_scan_fwd_ex(const void* x, const void* delta, const float* A, const void
   return scan_impl(x, delta, A, B, C, D, z, h0, y, h_last, batch, seqlen, d_inner, d_state, io_dtype, opts,
                    workspace, workspace_bytes, stream);
 }
+
+int ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                         const float* D, const void* z, const float* h0, void* y, float* h_last, int64_t batch,
+                         int64_t seqlen, int64_t d_inner, int64_t d_state, int32_t io_dtype,
+                         const ssm_scan_opts_t* opts, void* stream) {
+  return scan_impl(x, delta, A, B, C, D, z, h0, y, h_last, batch, seqlen, d_inner, d_state, io_dtype, opts, nullptr, 0,
+                   stream, true);
+}
+
+size_t ssm_scan_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
 
 int ssm_state_update(float* h, const void* x_t, const void* delta_t, const float* A, const void* B_t,
                      const void* C_t, const float* D, const void* z_t, void* y_t, int64_t batch, int64_t d_inner,

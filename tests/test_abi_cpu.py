@@ -93,6 +93,24 @@ def test_scan_argument_errors(lib):
     assert _scan(lib, opts=o, ws=P0 + 8 * MB, ws_bytes=need) == bd.SSM_ERR_ALIAS
 
 
+def test_noalloc_scan_checks_before_any_launch(lib):
+    """ssm_scan_fwd_noalloc validates like ssm_scan_fwd_ex, and an explicit
+    chunk length whose carries exceed its scratch is refused on the host."""
+    GB = 1 << 30
+    assert lib.ssm_scan_fwd_noalloc_max_bytes() == 64 << 20
+
+    def na(batch, L, d, N, chunk_len, x=P0, dtype=1):
+        o = bd.ScanOpts(0, 0, chunk_len, 0, 0, None, None)
+        return lib.ssm_scan_fwd_noalloc(x, P0 + GB, P0 + 2 * GB, P0 + 3 * GB, P0 + 4 * GB, None, None, None,
+                                        P0 + 8 * GB, None, batch, L, d, N, dtype, ctypes.byref(o), None)
+    assert na(2, 4, 8, 16, 0, x=None) == bd.SSM_ERR_NULL_ARG
+    assert na(2, 4, 8, 3, 0) == bd.SSM_ERR_UNSUPPORTED
+    assert na(2, 4, 8, 16, 0, x=P0 + 1) == bd.SSM_ERR_MISALIGNED
+    # 16 chunks of 8 steps at 64 x 4096 x 16 states: 46 * 4M floats = 736 MiB of carries.
+    assert na(64, 128, 4096, 16, 8) == bd.SSM_ERR_WORKSPACE
+    assert na(64, 128, 4096, 16, 8, dtype=0) == bd.SSM_ERR_WORKSPACE
+
+
 def test_empty_scans_return_before_any_launch(lib):
     assert _scan(lib, batch=0, x=None, delta=None, y=None, B=None, C=None) == bd.SSM_OK
     assert _scan(lib, d=0, x=None, delta=None, y=None, A=None) == bd.SSM_OK
