@@ -3,17 +3,26 @@
 
 One step = one ssm_scan_fwd call over a whole Mamba layer's batch (all of the
 scan's steps: load and unpack, decay, input term, recurrence, readout, gate,
-store, final state), with inputs already resident in HBM.  The default
+store, final state), with inputs already resident in HBM.  The headline
 workload is the Mamba-1.4B layer shape (batch 32, L 4096, d_inner 4096,
-d_state 16, bf16 io, fp32 state).  The same run also times, each on its own
-line of the JSON object: the scan's backward pass (standalone, and the
-training path where the forward saves state checkpoints), the causal conv1d
-that feeds the scan, the decode update (256 sequences x 5120 channels x 16
-states, 1000 consecutive in-place steps), and the fp64 CPU oracle on a
-bounded sample of the scan workload.  Prints one JSON line.
+d_state 16, bf16 io, fp32 state) on the general path (the plain entry point:
+one exponential per state), measured against the HBM roofline.  The same JSON
+line also carries, each as its own object:
+  * structured_a: the same layer with SSM_FLAG_A_LINEAR_N (its A = -(n+1)
+    has that structure);
+  * scan_c4 / scan_c2: the Mamba-2.8B long-context layer (batch 4, L 32768,
+    d_inner 5120, h0 != 0) and the Mamba-130M layer, general and structured,
+    with whole-row parity against the oracle;
+  * parity_channel_params: the 1.4B layer's inputs with random per-channel A
+    and D, whole rows against the oracle;
+  * the scan's backward pass, the causal conv1d, the decode update (256 x
+    5120 x 16 state, 1000 in-place steps), the Mamba-2 SSD form, and the fp64
+    CPU oracle on a bounded sample of the headline workload (cpu_baseline).
+Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-decode] [--no-conv] [--no-bwd] [--no-ssd] [--no-cpu-baseline]
+                       [--no-extra-scans]
 """
 import argparse
 import hashlib
@@ -34,8 +43,15 @@ VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 # are half rate: 2 slots).  Per state: mul (delta*A), exp (2), mul (delta*x*B),
 # FMA (state), FMA (readout) = 6.  Per element: widen x, widen delta,
 # delta*x, D*x, widen z, -z*log2e, exp (2), +1, rcp (2), z*r, y*silu, narrow y.
-def scan_slots_per_element(d_state: int) -> int:
-    return 6 * d_state + 14
+def scan_slots_per_element(d_state: int, linear_a: bool = False) -> int:
+    if not linear_a:
+        return 6 * d_state + 14
+    # Structured A (one wave per tile): exp2 at y, 2y, 4y, 8y, 16y (2 slots
+    # each) with their scalings, y = delta * A[d, 0] log2 e, the other decays
+    # as one product each; per state mul (delta*x*B), FMA (state), FMA (readout).
+    n = min(d_state, 16)
+    exps = 1 + (n > 1) + (n > 3) + (n > 7) + (n > 15)
+    return 2 * exps + (exps - 1) + 1 + (n - exps) + 3 * d_state + 14
 
 
 # Minimum VALU slots per element of the scan's backward pass with the decays
@@ -101,15 +117,18 @@ def to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def bench_scan(cfg, steps, warmup, dev, n_split=0, chunk_len=0, flags=0):
+def bench_scan(cfg, steps, warmup, dev, n_split=0, chunk_len=0, flags=0, inp=None, d=None):
+    """Times ssm_scan_fwd on cfg's workload (inputs generated unless given)."""
     import torch
     from selective_state_space_84_amd import binding, inputs
     t0 = time.time()
     softplus = bool(flags & binding.SSM_FLAG_DELTA_SOFTPLUS)
-    inp = inputs.make_scan_inputs(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, cfg.seed,
-                                  cfg.nonzero_h0, raw_delta=softplus)
+    if inp is None:
+        inp = inputs.make_scan_inputs(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, cfg.seed,
+                                      cfg.nonzero_h0, raw_delta=softplus)
     gen_s = time.time() - t0
-    d = {k: to_dev(inp.get(k), dev) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "dt_bias")}
+    if d is None:
+        d = {k: to_dev(inp.get(k), dev) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "dt_bias")}
     y = torch.empty_like(d["x"])
     hl = torch.empty((cfg.batch, cfg.d_inner, cfg.d_state), dtype=torch.float32, device=dev)
     g, chunk_len, n_chunks = binding.scan_plan(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, n_split, chunk_len,
@@ -156,7 +175,102 @@ def bench_scan(cfg, steps, warmup, dev, n_split=0, chunk_len=0, flags=0):
     spread = {"median": round(per[len(per) // 2], 6), "min": round(per[0], 6), "max": round(per[-1], 6)}
     step(0)  # y, hl of the first set (every set holds the same inputs)
     torch.cuda.synchronize()
-    return inp, y, hl, ms, gen_s, (g, chunk_len, n_chunks, len(sets)), spread
+    del sets
+    return inp, d, y, hl, ms, gen_s, (g, chunk_len, n_chunks), spread
+
+
+def scan_record(cfg, ms, spread, plan, flags, h0):
+    """Throughput, HBM and VALU-slot figures of one timed scan leg."""
+    from selective_state_space_84_amd import binding
+    el = cfg.batch * cfg.seqlen * cfg.d_inner
+    io_bytes = 2 if cfg.dtype == "bf16" else 4
+    alg = algorithmic_scan_bytes(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, io_bytes, h0, True)
+    linear = bool(flags & binding.SSM_FLAG_A_LINEAR_N)
+    slots = scan_slots_per_element(cfg.d_state, linear)
+    el_s = el / (ms * 1e-3)
+    gbps = alg / (ms * 1e-3) / 1e9
+    g, chunk_len, n_chunks = plan
+    return {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "d_inner": cfg.d_inner,
+            "d_state": cfg.d_state, "io_dtype": cfg.dtype, "h0": bool(h0),
+            "path": "structured A (SSM_FLAG_A_LINEAR_N)" if linear else "general A",
+            "n_split": g, "chunk_len": chunk_len, "n_chunks": n_chunks,
+            "ms_per_step": round(ms, 6), "step_ms": spread, "elements_per_s": round(el_s, 1),
+            "algorithmic_bytes": alg, "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "valu_slots_per_element": slots,
+            "valu_frac": round(el_s * slots / 1e12 / VALU_PEAK_TSLOTS, 4),
+            "note": "valu_frac counts the unchunked sweep's minimum slots; a chunked plan also runs a summary "
+                    "sweep over all chunks but the last" if n_chunks > 1 else ""}
+
+
+def _host_f64(t):
+    import numpy as np
+    import torch
+    from selective_state_space_84_amd.inputs import bf16_bits_to_f32
+    if t.dtype == torch.bfloat16:
+        return bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def _floored(g, r):
+    import numpy as np
+    floor = 0.1 * float(np.sqrt(np.mean(r * r)))
+    return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), floor)))
+
+
+def oracle_rows(cfg, inp, rows, flags=0, width=256):
+    """Oracle y[b] (L, d_inner) and h_last[b] for whole batch rows, channel slices on threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    out = {}
+
+    def run_slice(b, c0):
+        c1 = min(cfg.d_inner, c0 + width)
+        sl, c = slice(b, b + 1), slice(c0, c1)
+        return oracle.scan(inp["x"][sl, :, c], inp["delta"][sl, :, c], inp["A"][c], inp["B"][sl], inp["C"][sl],
+                           inp["D"][c], inp["z"][sl, :, c], None if inp.get("h0") is None else inp["h0"][sl, c],
+                           inp["dt_bias"][c] if flags & 1 else None, exact_zoh=bool(flags & 2),
+                           delta_softplus=bool(flags & 1))
+
+    with ThreadPoolExecutor(_host_threads()) as ex:
+        for b in rows:
+            parts = list(ex.map(lambda c0: run_slice(b, c0), range(0, cfg.d_inner, width)))
+            out[b] = (np.concatenate([p[0][0] for p in parts], axis=1),
+                      np.concatenate([p[1][0] for p in parts], axis=0))
+    return out
+
+
+def row_parity(cfg, inp, y, hl, rows, flags=0):
+    """Floored errors of whole GPU rows against the oracle."""
+    ref = oracle_rows(cfg, inp, rows, flags)
+    ey = max(_floored(_host_f64(y[b]), ref[b][0]) for b in rows)
+    eh = max(_floored(_host_f64(hl[b]), ref[b][1]) for b in rows)
+    return {"rows_checked": list(rows), "y_err": ey, "h_last_err": eh,
+            "gate": 2e-2 if cfg.dtype == "bf16" else 1e-5,
+            "metric": "max |g-r| / max(|r|, 0.1 rms(r)) vs fp64 oracle, whole rows"}
+
+
+def bench_layer(cfg, steps, warmup, dev, rows, structured=True):
+    """General and structured scan legs on one layer shape, with row parity."""
+    import torch
+    from selective_state_space_84_amd import binding
+    inp, d, y, hl, ms, gen_s, plan, spread = bench_scan(cfg, steps, warmup, dev)
+    rec = {"general": scan_record(cfg, ms, spread, plan, 0, inp["h0"] is not None), "input_gen_s": round(gen_s, 1)}
+    rec["general"]["parity"] = row_parity(cfg, inp, y, hl, rows)
+    if structured:
+        lin = binding.SSM_FLAG_A_LINEAR_N
+        _, _, y2, hl2, ms2, _, plan2, spread2 = bench_scan(cfg, steps, warmup, dev, flags=lin, inp=inp, d=d)
+        rec["structured_a"] = scan_record(cfg, ms2, spread2, plan2, lin, inp["h0"] is not None)
+        par = row_parity(cfg, inp, y2, hl2, rows)
+        par["vs_general_all_rows"] = {"y_err": max(_floored(_host_f64(y2[b]), _host_f64(y[b])) for b in range(cfg.batch)),
+                                      "h_last_err": _floored(_host_f64(hl2), _host_f64(hl))}
+        rec["structured_a"]["parity"] = par
+        del y2, hl2
+    del y, hl, d
+    torch.cuda.empty_cache()
+    return rec
 
 
 def bench_decode(steps, dev):
@@ -421,6 +535,14 @@ def cpu_baseline(cfg, inp, y_dev, hl_dev, cpu_budget_s=24.0, flags=0):
         "metric": "max |g-r| / max(|r|, 0.1 rms(r)) vs fp64 oracle", "gate": 2e-2 if cfg.dtype == "bf16" else 1e-5}
 
 
+def log(msg):
+    """Progress on stderr (stdout carries only the JSON line)."""
+    print("[bench %6.1fs] %s" % (time.time() - _T0, msg), file=sys.stderr, flush=True)
+
+
+_T0 = time.time()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -434,9 +556,12 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-scans", action="store_true",
+                    help="skip the structured-A, 2.8B-long, 130M and per-channel-parameter legs")
     ap.add_argument("--n-split", type=int, default=0, help="override the launch plan (tuning)")
     ap.add_argument("--chunk-len", type=int, default=0, help="override the launch plan (tuning)")
-    ap.add_argument("--flags", default="", help="comma list: softplus (fused softplus step), zoh (exact ZOH)")
+    ap.add_argument("--flags", default="",
+                    help="comma list: softplus (fused softplus step), zoh (exact ZOH), linear (structured A)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -449,26 +574,26 @@ def main():
     dev = "cuda:0"
     binding.load_library()
     cfg = inputs.SCAN_CONFIGS[args.workload]
-    flag_bits = {"softplus": binding.SSM_FLAG_DELTA_SOFTPLUS, "zoh": binding.SSM_FLAG_EXACT_ZOH}
+    flag_bits = {"softplus": binding.SSM_FLAG_DELTA_SOFTPLUS, "zoh": binding.SSM_FLAG_EXACT_ZOH,
+                 "linear": binding.SSM_FLAG_A_LINEAR_N}
     flag_names = [f for f in args.flags.split(",") if f]
     unknown = [f for f in flag_names if f not in flag_bits]
     if unknown:
         ap.error("unknown --flags %s (known: %s)" % (",".join(unknown), ",".join(flag_bits)))
     flags = sum(flag_bits[f] for f in flag_names)
-    inp, y, hl, ms, gen_s, (g, chunk_len, n_chunks, n_sets), spread = bench_scan(cfg, args.steps, args.warmup, dev,
-                                                                       args.n_split, args.chunk_len, flags)
-    el = cfg.batch * cfg.seqlen * cfg.d_inner
-    io_bytes = 2 if cfg.dtype == "bf16" else 4
-    alg_bytes = algorithmic_scan_bytes(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, io_bytes,
-                                       inp["h0"] is not None, True)
-    el_per_s = el / (ms * 1e-3)
-    gbps = alg_bytes / (ms * 1e-3) / 1e9
-    slots = scan_slots_per_element(cfg.d_state)
-    achieved_slots = el_per_s * slots / 1e12
+    log("headline: %s scan, flags %d" % (cfg.name, flags))
+    inp, d, y, hl, ms, gen_s, plan, spread = bench_scan(cfg, args.steps, args.warmup, dev, args.n_split,
+                                                        args.chunk_len, flags)
+    g, chunk_len, n_chunks = plan
+    rec = scan_record(cfg, ms, spread, plan, flags, inp["h0"] is not None)
+    alg_bytes = rec["algorithmic_bytes"]
+    gbps = rec["hbm_gbps"]
+    slots = rec["valu_slots_per_element"]
+    achieved_slots = rec["elements_per_s"] * slots / 1e12
     sha = _kernel_source_sha("scan")
     out = {
         "metric": "selective-scan elements/s (B·L·d_inner) and achieved HBM GB/s vs peak",
-        "value": round(el_per_s, 1),
+        "value": rec["elements_per_s"],
         "unit": "elements/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -479,39 +604,80 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "io_dtype": cfg.dtype,
         "data": "synthetic (seeded; Mamba layer init distributions)",
         "config": {"workload": cfg.name + " scan", "batch": cfg.batch, "seqlen": cfg.seqlen,
                    "d_inner": cfg.d_inner, "d_state": cfg.d_state, "io_dtype": cfg.dtype, "state_dtype": "f32",
-                   "h0": inp["h0"] is not None, "n_split": g, "n_chunks": n_chunks, "input_sets": n_sets,
-                   "variant": "+".join(flag_names) or "plain"},
-        "hbm_gbps": round(gbps, 1),
-        "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "alu", "achieved": round(achieved_slots, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
-                     "unit": "Tslot/s", "frac": round(achieved_slots / VALU_PEAK_TSLOTS, 4),
-                     "traffic": _traffic(cfg.name, sha) if n_chunks == 1 else None,
-                     "slots_per_element": slots, "kernel": "k_scan_sweep (one launch per step)"},
-        "roofline_hbm": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": alg_bytes},
+                   "h0": inp["h0"] is not None, "n_split": g, "n_chunks": n_chunks,
+                   "variant": "+".join(flag_names) or "plain (general A)"},
+        "hbm_gbps": gbps,
+        "hbm_frac_of_peak": rec["hbm_frac"],
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": rec["hbm_frac"],
+                     "traffic": _traffic(cfg.name, sha) if n_chunks == 1 and not flags else None,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "kernel": "k_scan_sweep (one launch per step)" if n_chunks == 1 else
+                               "k_scan_sweep summary + k_chunk_carry + k_scan_sweep (per step)"},
+        "roofline_alu": {"bound": "alu", "achieved": round(achieved_slots, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
+                         "unit": "Tslot/s", "frac": round(achieved_slots / VALU_PEAK_TSLOTS, 4),
+                         "slots_per_element": slots,
+                         "note": "VALU issue slots of the sweep (exp and rcp 2 slots, non-packed fp32): the "
+                                 "bound this general-A scan actually meets; HBM is ~1/3 used"},
         "kernel_source_sha": sha,
         "input_gen_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:
+        log("cpu baseline")
         cb, par = cpu_baseline(cfg, inp, y, hl, flags=flags)
         out["cpu_baseline"] = cb
         out["parity"] = par
-    del y, hl
+    extra = not args.no_extra_scans and args.workload == "mamba-1.4b-layer" and not flags
+    if extra:
+        lin = binding.SSM_FLAG_A_LINEAR_N
+        log("structured A on the headline workload")
+        _, _, y2, hl2, ms2, _, plan2, spread2 = bench_scan(cfg, args.steps, args.warmup, dev, flags=lin, inp=inp, d=d)
+        sa = scan_record(cfg, ms2, spread2, plan2, lin, inp["h0"] is not None)
+        sa["roofline"] = {"bound": "hbm", "achieved": sa["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": sa["hbm_frac"], "algorithmic_bytes_per_launch": sa["algorithmic_bytes"]}
+        rows = [0, cfg.batch - 1]
+        sa["parity"] = row_parity(cfg, inp, y2, hl2, rows)
+        sa["parity"]["vs_general_all_rows"] = {
+            "y_err": max(_floored(_host_f64(y2[b]), _host_f64(y[b])) for b in range(cfg.batch)),
+            "h_last_err": _floored(_host_f64(hl2), _host_f64(hl))}
+        out["structured_a"] = sa
+        del y2, hl2
+        log("per-channel parameters on the headline workload")
+        A, Dv = inputs.channel_params(cfg.d_inner, cfg.d_state, cfg.seed, "random")
+        d["A"], d["D"] = to_dev(A, dev), to_dev(Dv, dev)
+        pin = dict(inp, A=A, D=Dv)
+        yp, hp = binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"])
+        torch.cuda.synchronize()
+        out["parity_channel_params"] = dict(row_parity(cfg, pin, yp, hp, rows),
+                                            params="A[d,n] = -(n+1) exp(U[-0.5,0.5]), D ~ N(1, 0.5)")
+        del yp, hp
+    del y, hl, d
     torch.cuda.empty_cache()
+    if extra:
+        log("mamba-2.8b long layer")
+        out["scan_c4"] = bench_layer(inputs.MAMBA_2P8B_LONG, max(3, args.steps // 2), args.warmup, dev, rows=[1])
+        log("mamba-130m layer")
+        out["scan_c2"] = bench_layer(inputs.MAMBA_130M, args.steps, args.warmup, dev, rows=[0, 7])
     if not args.no_bwd and cfg.d_state <= 16:
-        out["scan_bwd"] = bench_bwd(cfg, inp, max(1, args.steps // 2), dev, flags)
+        log("backward")
+        out["scan_bwd"] = bench_bwd(cfg, inp, max(1, args.steps // 2), dev, flags & 3)
         torch.cuda.empty_cache()
     if not args.no_conv:
+        log("conv1d")
         out["conv1d"] = bench_conv(cfg, args.steps, dev)
         torch.cuda.empty_cache()
     if not args.no_decode:
+        log("decode")
         out["decode"] = bench_decode(args.decode_steps, dev)
         torch.cuda.empty_cache()
     if not args.no_ssd:
+        log("ssd")
         out["ssd"] = bench_ssd(args.steps, dev)
+    log("done")
     print(json.dumps(out), flush=True)
 
 

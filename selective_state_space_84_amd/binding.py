@@ -19,6 +19,7 @@ SSM_DTYPE_F32 = 0
 SSM_DTYPE_BF16 = 1
 SSM_FLAG_DELTA_SOFTPLUS = 0x1
 SSM_FLAG_EXACT_ZOH = 0x2
+SSM_FLAG_A_LINEAR_N = 0x4
 
 SSM_OK = 0
 SSM_ERR_NULL_ARG = -1

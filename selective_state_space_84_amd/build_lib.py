@@ -15,7 +15,8 @@ REPO = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(REPO, "include")
 LIB = os.path.join(HERE, "libssm_scan.so")
-SOURCES = ["scan_mode0.hip", "scan_mode1.hip", "scan_mode2.hip", "scan_mode3.hip", "scan_aux.hip",
+SOURCES = ["scan_mode0.hip", "scan_mode1.hip", "scan_mode2.hip", "scan_mode3.hip", "scan_mode4.hip", "scan_mode5.hip",
+           "scan_mode6.hip", "scan_mode7.hip", "scan_aux.hip",
            "update_kernel.hip", "conv_kernels.hip", "scan_bwd.hip", "ssd_kernel.hip", "abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

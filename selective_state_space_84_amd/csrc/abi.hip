@@ -31,7 +31,7 @@ constexpr int64_t kChunkTargetWaves = 16384;
 constexpr int64_t kMinAutoChunk = 64;
 // Workspace alignment the library asks for.
 constexpr uintptr_t kWorkspaceAlign = 256;
-constexpr uint32_t kKnownFlags = SSM_FLAG_DELTA_SOFTPLUS | SSM_FLAG_EXACT_ZOH;
+constexpr uint32_t kKnownFlags = SSM_FLAG_DELTA_SOFTPLUS | SSM_FLAG_EXACT_ZOH | SSM_FLAG_A_LINEAR_N;
 
 bool mul3(int64_t a, int64_t b, int64_t c, int64_t* out) {
   int64_t t;

@@ -59,11 +59,15 @@ hipError_t launch_state_fill(float* dst, const float* src, int64_t states, hipSt
 }
 
 hipError_t launch_scan(const ScanLaunch& p) {
-  switch (p.flags & 3u) {
+  switch (p.flags & 7u) {
     case 0: return launch_scan_mode<0>(p);
     case 1: return launch_scan_mode<1>(p);
     case 2: return launch_scan_mode<2>(p);
-    default: return launch_scan_mode<3>(p);
+    case 3: return launch_scan_mode<3>(p);
+    case 4: return launch_scan_mode<4>(p);
+    case 5: return launch_scan_mode<5>(p);
+    case 6: return launch_scan_mode<6>(p);
+    default: return launch_scan_mode<7>(p);
   }
 }
 

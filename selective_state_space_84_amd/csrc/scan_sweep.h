@@ -49,6 +49,12 @@
 //     principle to code" section 2.2) instead of delta * B; a = 0 takes the
 //     limit delta * B.  The coefficient comes from zoh_coef (ssm_device.h),
 //     accurate to about 3 ulp, including where delta * a is tiny.
+//   kLinearA: the caller asserts A[d, n] = (n + 1) A[d, 0] (the S4D-real
+//     family, "Mamba from principle to code" section 6.2, derivation page
+//     section 5.1: A_log = log(1..N), possibly shifted per channel).  Then
+//     abar_n = r^(n+1) with r = exp(delta A[d, 0]), and linear_decays
+//     evaluates the 16 decays of a state row from five exponentials and 11
+//     products instead of 16 exponentials; only A[d, 0] is read.
 #pragma once
 
 #include "ssm_device.h"
@@ -61,6 +67,28 @@ namespace {
 
 constexpr int kSoftplusDelta = 1;
 constexpr int kExactZoh = 2;
+constexpr int kLinearA = 4;
+
+// q[j] = 2^((j + 1) y) for j < NS (NS <= 16): r^(j+1) with r = 2^y.  exp2 is
+// evaluated at y, 2y, 4y, 8y and 16y (exact multiples) and every other power
+// is a product r^(2^k) * r^m of smaller ones (at most four exponentials and
+// three roundings in any power).  A plain chain r * r * ... would carry r's
+// rounding into r^16 sixteen times over, coherently in every state of the
+// element; emulated in fp32 with correctly rounded exp2 that costs the scan up
+// to 2.5e-5 against the oracle on 1000-step cases, exponentials at y, 4y, 16y
+// only still 1.3e-5 on one 64-step case (as measured on the device), and this
+// form the same errors as one exp2 per state.
+template <int NS>
+__device__ __forceinline__ void linear_decays(float y, float (&q)[NS]) {
+  static_assert(NS <= 16, "at most 16 states per wave");
+  q[0] = hw_exp2(y);
+#pragma unroll
+  for (int p = 2; p <= NS; p *= 2) {
+    q[p - 1] = hw_exp2((float)p * y);
+#pragma unroll
+    for (int m = 1; m < p && p + m <= NS; ++m) q[p + m - 1] = q[p - 1] * q[m - 1];
+  }
+}
 
 constexpr int kTB = kTimeBlock;
 // Steps ahead of the current block whose B/C lines are warmed into L2.
@@ -157,11 +185,13 @@ __global__ void __launch_bounds__(64 * (N / NS))
 
   float Al2[NS], h[NS];
   float ia[(MODE & kExactZoh) ? NS : 1];  // 1/a for the exact-ZOH coefficient
+  // With kLinearA only A[d, 0] is read: A[d, n] = (n + 1) A[d, 0].
+  const float Al2_1 = (MODE & kLinearA) ? A[dc * N] * kLog2e : 0.f;
   {
     const float* Ap = A + dc * N + n0;
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
-      const float a = Ap[n];
+      const float a = (MODE & kLinearA) ? (float)(n0 + n + 1) * A[dc * N] : Ap[n];
       Al2[n] = a * kLog2e;
       if (MODE & kExactZoh) ia[n] = 1.0f / a;
     }
@@ -303,10 +333,26 @@ __global__ void __launch_bounds__(64 * (N / NS))
       if (MODE & kSoftplusDelta) dv = softplus(dv, dtb);
       const float wx = dv * xv;
       float acc = Dv * xv;
+      float lin[(MODE & kLinearA) ? NS : 1];
+      if constexpr ((MODE & kLinearA) != 0) {
+        const float y1 = dv * Al2_1;
+        linear_decays<NS>(y1, lin);
+        if constexpr (G > 1) {
+          // Wave wv owns states n0 + 1 .. n0 + NS: scale r^(j+1) by r^n0.
+          const float base = hw_exp2(y1 * (float)n0);
+#pragma unroll
+          for (int n = 0; n < NS; ++n) lin[n] *= base;
+        }
+      }
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
         const float yv = dv * Al2[n];
-        const float ab = hw_exp2(yv);
+        float ab;
+        if constexpr ((MODE & kLinearA) != 0) {
+          ab = lin[n];
+        } else {
+          ab = hw_exp2(yv);
+        }
         if (MODE & kExactZoh) {
           const float coef = zoh_coef(yv, ab, dv, ia[n]);
           h[n] = __builtin_fmaf(coef, xv * bc.get(n), ab * h[n]);

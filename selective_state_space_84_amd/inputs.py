@@ -28,7 +28,10 @@ Recipe (the same for every consumer):
     ``SeedSequence([seed, 0xA11]).spawn(2)`` = [A, D], so the other tensors
     are the same as with the default ``params="s4d"``.  The parity tests use
     it so that every per-channel index of A and D is checked; the layer
-    configs keep the S4D-real initialisation.
+    configs keep the S4D-real initialisation.  ``params="linear"`` keeps the
+    S4D-real structure with a per-channel scale, A[d, n] = (n + 1) A[d, 0]
+    with A[d, 0] = -exp(U[-0.5, 0.5]) (rounded to fp32 before the multiple),
+    and D ~ N(1, 0.5): inputs for the structured-A path.
   * h0 ~ N(0, 0.1^2) per state when a nonzero initial state is asked for.
   * Values are drawn and computed in float64, rounded to float32 (nearest
     even), and for bf16 tensors rounded again to bfloat16 (nearest even).
@@ -131,6 +134,11 @@ def _inv_softplus(u: np.ndarray) -> np.ndarray:
     return np.log(np.expm1(u))
 
 
+def channel_params(d_inner: int, d_state: int, seed: int, params: str = "s4d"):
+    """(A, D) fp32 of make_scan_inputs(..., params=params) for these sizes and seed."""
+    return _channel_params(d_inner, d_state, seed, params)
+
+
 def _channel_params(d_inner: int, d_state: int, seed: int, params: str):
     """(A, D) fp32: the S4D-real initialisation, or random per-channel values."""
     if params == "s4d":
@@ -143,12 +151,17 @@ def _channel_params(d_inner: int, d_state: int, seed: int, params: str):
         A = round_to_f32(-(np.arange(1, d_state + 1, dtype=np.float64))[None, :] * scale)
         D = round_to_f32(1.0 + 0.5 * np.random.default_rng(kd).standard_normal(d_inner))
         return A, D
+    if params == "linear":
+        a0 = np.exp(np.random.default_rng(ka).uniform(-0.5, 0.5, d_inner))
+        A = round_to_f32(-(np.arange(1, d_state + 1, dtype=np.float64))[None, :] * round_to_f32(a0)[:, None])
+        D = round_to_f32(1.0 + 0.5 * np.random.default_rng(kd).standard_normal(d_inner))
+        return A, D
     if params == "wide":
         a = np.exp(np.random.default_rng(ka).standard_normal((d_inner, d_state)))
         A = round_to_f32(-np.clip(a, 0.05, 20.0))
         D = round_to_f32(np.random.default_rng(kd).standard_normal(d_inner))
         return A, D
-    raise ValueError("params must be 's4d', 'random' or 'wide', got %r" % (params,))
+    raise ValueError("params must be 's4d', 'random', 'linear' or 'wide', got %r" % (params,))
 
 
 def _threads(threads: Optional[int]) -> int:

@@ -40,3 +40,11 @@ def test_traffic_follows_the_kernel_sources():
         pytest.skip("the scan kernel changed since its traffic counters were taken")
     # Measured traffic sits within a few percent of the algorithmic bytes.
     assert abs(got / 4312023040 - 1) < 0.05
+
+
+def test_valu_slot_model():
+    # General A: 6 slots per state (mul, exp = 2, mul, two FMAs) + 14 per element.
+    assert bench.scan_slots_per_element(16) == 110
+    # Structured A: exp2 at y, 2y, 4y, 8y, 16y (2 slots each), four scalings,
+    # y itself, 11 products, then 3 slots per state + 14 per element.
+    assert bench.scan_slots_per_element(16, linear_a=True) == 10 + 4 + 1 + 11 + 48 + 14 == 88
