@@ -256,7 +256,7 @@ int ssm_state_update_ex(float* h, const void* x_t, const void* delta_t, const fl
 /*
  * Workspace bytes ssm_scan_bwd needs for these sizes (state checkpoints every
  * 8 steps plus per-tile partial sums: about 8 bytes per (b, t, d) element for
- * d_state 16).  Returns (size_t)-1 for invalid or unsupported sizes.  Pure
+ * d_state 16, and 12 more per element above 16 states).  Returns (size_t)-1 for invalid or unsupported sizes.  Pure
  * host computation.
  */
 size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state);
@@ -306,7 +306,10 @@ size_t ssm_scan_bwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_i
  *                 the forward call.  With the exact ZOH, B's coefficient
  *                 (exp(delta a) - 1)/a is differentiated in both delta (its
  *                 derivative is abar) and a.
- *   d_state     : 2, 4, 8 or 16.
+ *   d_state     : 2, 4, 8, 16, 32, 64 or 128.  Above 16 the states are
+ *                 handled in groups of 16 (one sweep per group) and the
+ *                 workspace holds 12 more bytes per (b, t, d) element for the
+ *                 groups' per-element sums.
  *   workspace   : at least ssm_scan_bwd_workspace_size() bytes (or
  *                 ssm_scan_bwd_workspace_size_ex(..., 1) when ckpt is given),
  *                 256-byte aligned; contents on entry ignored.

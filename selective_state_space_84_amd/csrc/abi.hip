@@ -339,7 +339,7 @@ int update_impl(float* h, const void* x_t, const void* delta_t, const float* A, 
   return ssm::launch_update(p) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
-bool bwd_d_state_ok(int64_t n) { return n == 2 || n == 4 || n == 8 || n == 16; }
+bool bwd_d_state_ok(int64_t n) { return n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64 || n == 128; }
 
 // Floats of backward workspace, or -1 when a size overflows.
 int64_t bwd_workspace_floats(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, bool ckpt_given) {
@@ -350,7 +350,9 @@ int64_t bwd_workspace_floats(int64_t batch, int64_t seqlen, int64_t d_inner, int
   if (!mul3(batch, nblk, d_state, &a) || __builtin_mul_overflow(a, d_inner, &a)) return -1;
   if (!mul3(tiles, batch, seqlen, &b) || __builtin_mul_overflow(b, 2 * d_state, &b)) return -1;
   if (!mul3(batch, d_inner, d_state, &c)) return -1;
-  if (a > INT64_MAX / 8 || b > INT64_MAX / 8 || c > INT64_MAX / 8) return -1;
+  int64_t el;  // per-element sums of the state groups (d_state > 16): 3 floats per element
+  if (!mul3(batch, seqlen, d_inner, &el)) return -1;
+  if (a > INT64_MAX / 8 || b > INT64_MAX / 8 || c > INT64_MAX / 8 || el > INT64_MAX / 16) return -1;
   int64_t total;
   ssm::bwd_workspace_layout(nullptr, batch, seqlen, d_inner, d_state, ssm::bwd_plan(batch, seqlen, d_inner), ckpt_given,
                             &total);

@@ -127,11 +127,13 @@ __device__ __forceinline__ float to_io<float>(float v) {
 // accumulated as the product of the very decays the sweep multiplies lam by:
 // for slowly decaying channels (small delta) this matches the unsplit sweep
 // far more closely than exp of the rounded sum.
-template <typename T, int N, int MODE>
+// NF is the full state count of the tensors (A rows, B/C rows, lP/lS): a
+// launch with N < NF covers states n_off .. n_off + N - 1 of them.
+template <typename T, int N, int MODE, int NF = N>
 __global__ void __launch_bounds__(64)
     k_bwd_lam_summary(const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ C,
                       const T* __restrict__ z, const T* __restrict__ dy, const float* __restrict__ dt_bias,
-                      float* __restrict__ lP, float* __restrict__ lS, const BwdDims dm) {
+                      float* __restrict__ lP, float* __restrict__ lS, const BwdDims dm, const int n_off) {
   const int lane = threadIdx.x;
   int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = bid % dm.tiles;
@@ -152,7 +154,7 @@ __global__ void __launch_bounds__(64)
   float Al2[N], lam[N], P[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    Al2[n] = A[dc * N + n] * kLog2e;
+    Al2[n] = A[dc * NF + n_off + n] * kLog2e;
     lam[n] = 0.f;
     P[n] = 1.f;
   }
@@ -163,7 +165,7 @@ __global__ void __launch_bounds__(64)
   auto rs = [&](const void* base, int64_t t) {
     return block_rsrc(reinterpret_cast<const char*>(base) + ((b * L + t) * DI + cbase) * (int64_t)sizeof(T), blk_span);
   };
-  const T* Cb = C + b * L * N;
+  const T* Cb = C + b * L * NF + n_off;
   // Blocks run from the chunk's end backwards.  The raw delta / dy / z rows
   // of the next (earlier) block load while the current one computes, and
   // each step's C row is requested one step ahead through SGPRs.
@@ -183,7 +185,7 @@ __global__ void __launch_bounds__(64)
   StateRow<T, N> cq;
   if (t_hi > t_lo) {
     fetch(t_hi);
-    cq.load(Cb + (t_hi - 1) * N);
+    cq.load(Cb + (t_hi - 1) * NF);
   }
   for (int64_t t1 = t_hi; t1 > t_lo; t1 -= kBB) {
     const int64_t t0 = max(t_lo, t1 - kBB);
@@ -213,7 +215,7 @@ __global__ void __launch_bounds__(64)
         __builtin_amdgcn_sched_barrier(0);
         const StateRow<T, N> cr = cq;
         const int64_t t = t0 + i;
-        cq.load(Cb + (t > t_lo ? t - 1 : t) * N);  // at the chunk start: repeat the row
+        cq.load(Cb + (t > t_lo ? t - 1 : t) * NF);  // at the chunk start: repeat the row
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < N; ++n) {
@@ -226,7 +228,7 @@ __global__ void __launch_bounds__(64)
   }
   if (t_hi > t_lo) cq.touch();  // let the last row request land
   if (dvalid) {
-    const int64_t o = (((int64_t)(chunk - 1) * dm.batch + b) * DI + d) * N;
+    const int64_t o = (((int64_t)(chunk - 1) * dm.batch + b) * DI + d) * NF + n_off;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
       lP[o + n] = P[n];
@@ -280,7 +282,17 @@ constexpr int bwd_sub() {
 // Compiled for two waves per SIMD (256 VGPRs).  The exact-ZOH variant at 16
 // states spills ~130 B per lane at that size and is still faster than at one
 // wave per SIMD without spills.
-template <typename T, int N, int MODE>
+//
+// State groups (NF > N): with more states than fit one lane's registers the
+// sweep runs once per group of N states, n_off .. n_off + N - 1 of the NF in
+// the tensors.  The per-state results (lam, dA, dB, dC, dh0) are the group's
+// own; the per-element ones are sums over every state, so each group adds its
+// part, in fp32, to part_el = [3][batch][seqlen][d_inner]: the readout
+// sum_n C h (for dz), sum_n lam dt B (for dx) and the delta gradient before
+// the softplus factor.  The first group writes, the others add (the groups
+// run one after another on the stream); k_bwd_finalize then adds the skip and
+// gate terms and writes dx, ddelta, dz, and the dD and dt-bias partials.
+template <typename T, int N, int MODE, int NF = N>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     k_bwd_sweep(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
                 const T* __restrict__ B, const T* __restrict__ C, const float* __restrict__ D,
@@ -288,7 +300,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 const float* __restrict__ dt_bias, const float* __restrict__ ckpt, T* __restrict__ dx,
                 T* __restrict__ ddelta, T* __restrict__ dz, float* __restrict__ dh0, float* __restrict__ part_bc,
                 float* __restrict__ part_a, float* __restrict__ part_d, float* __restrict__ part_t,
-                const float* __restrict__ lam_in, const BwdDims dm) {
+                const float* __restrict__ lam_in, const BwdDims dm, const int n_off,
+                float* __restrict__ part_el) {
+  constexpr bool kPart = NF > N;
   constexpr int SUB = bwd_sub<N>();                   // steps of w held at once
   constexpr int NSUB = kBB / SUB;                     // sub-blocks per block
   constexpr int GS = (64 / N) < SUB ? (64 / N) : SUB;  // steps per LDS reduction group
@@ -313,14 +327,14 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
   // Lanes past d_inner run on a copy of the last channel with g = 0 and
   // lam = 0, so every term they add to the channel sums is zero.  The
   // incoming adjoint is dh_last for one chunk, else the chunk's carry.
-  const float* li = lam_in != nullptr ? lam_in + (((int64_t)chunk * dm.batch + b) * DI + d) * N
-                                      : (dh_last != nullptr ? dh_last + (b * DI + d) * N : nullptr);
+  const float* li = lam_in != nullptr ? lam_in + (((int64_t)chunk * dm.batch + b) * DI + d) * NF + n_off
+                                      : (dh_last != nullptr ? dh_last + (b * DI + d) * NF + n_off : nullptr);
   float Al2[N], lam[N], gA[N];
   float ia[(MODE & kExactZoh) ? N : 1];  // 1/a for the exact-ZOH coefficient
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    Al2[n] = A[dc * N + n] * kLog2e;
-    if (MODE & kExactZoh) ia[n] = 1.0f / A[dc * N + n];
+    Al2[n] = A[dc * NF + n_off + n] * kLog2e;
+    if (MODE & kExactZoh) ia[n] = 1.0f / A[dc * NF + n_off + n];
     lam[n] = (dvalid && li != nullptr) ? li[n] : 0.f;
     gA[n] = 0.f;
   }
@@ -340,17 +354,23 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                       0xffffffffu);
   };
   auto st = [&](__amdgpu_buffer_rsrc_t r, uint32_t so, float v) { buf_st(to_io<T>(v), r, lane_b, so); };
-  const T* Bb = B + b * L * N;
-  const T* Cb = C + b * L * N;
-  float* pbc = part_bc + ((int64_t)tile * dm.batch + b) * L * (2 * N);
+  const T* Bb = B + b * L * NF + n_off;
+  const T* Cb = C + b * L * NF + n_off;
+  float* pbc = part_bc + ((int64_t)tile * dm.batch + b) * L * (2 * NF) + n_off;
+  // fp32 per-element sums of a state group (plane 0 readout, 1 dx, 2 ddelta).
+  const int64_t plane = dm.batch * L * DI;
+  auto add_part = [&](int pl, int64_t t, float v) {
+    float* q = part_el + pl * plane + (b * L + t) * DI + d;
+    *q = n_off == 0 ? v : *q + v;
+  };
 
   // B/C rows run one step ahead through SGPRs: each step waits for its own
   // rows (issued one step earlier), then requests the rows of the step that
   // follows it in processing order.
   StateRow<T, N> bq, cq;
   auto issue = [&](int64_t t) {
-    bq.load(Bb + t * N);
-    cq.load(Cb + t * N);
+    bq.load(Bb + t * NF);
+    cq.load(Cb + t * NF);
     __builtin_amdgcn_sched_barrier(0);
   };
   auto take = [&](StateRow<T, N>& bc, StateRow<T, N>& cc) {
@@ -385,7 +405,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         __builtin_amdgcn_sched_barrier(0);
       }
       const int st_ = lane / N, n = lane % N;
-      if (g0 + st_ < nt) pbc[(t0 + g0 + st_) * (2 * N) + which + n] = (s0 + s1) + (s2 + s3);
+      if (g0 + st_ < nt) pbc[(t0 + g0 + st_) * (2 * NF) + which + n] = (s0 + s1) + (s2 + s3);
     }
     __syncthreads();
   };
@@ -427,7 +447,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     // for the block, the lane's column in a VGPR and the row offset in an
     // SGPR that is advanced per state (the empty asm keeps the compiler from
     // precomputing all N row offsets, which would hold 2N SGPRs).
-    const __amdgpu_buffer_rsrc_t cpr = block_rsrc(ckpt + (b * dm.nblk + k) * N * DI + cbase, 0xffffffffu);
+    const __amdgpu_buffer_rsrc_t cpr =
+        block_rsrc(ckpt + ((b * dm.nblk + k) * NF + n_off) * DI + cbase, 0xffffffffu);
     uint32_t so = 0;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
@@ -518,7 +539,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
               take(br, cr);
               issue(i + 1 < hi ? t0 + i + 1 : t0 + hi - 1);
               const float dtx = dtp[i] * xv[i];
-              float acc = Dv * xv[i];
+              float acc = kPart ? 0.f : Dv * xv[i];
 #pragma unroll
               for (int n = 0; n < N; ++n) {
                 if (MODE & kExactZoh) {
@@ -535,10 +556,14 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 acc = __builtin_fmaf(cr.get(n), h[n], acc);
                 red[(s * N + n) * kRedStride + lane] = g[ii] * h[n];
               }
-              if (has_z && dvalid) st(zo, (uint32_t)i * row_bytes, acc * dsz[ii]);
+              if constexpr (kPart) {
+                if (has_z && dvalid) add_part(0, t0 + i, acc);
+              } else {
+                if (has_z && dvalid) st(zo, (uint32_t)i * row_bytes, acc * dsz[ii]);
+              }
             }
           }
-          reduce(t0, lo + g0, nt, N);
+          reduce(t0, lo + g0, nt, NF);
         }
       }
 
@@ -589,15 +614,22 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 lam[n] *= hw_exp2(dti * Al2[n]);
               }
             }
-            const float dxv =
-                (MODE & kExactZoh) ? __builtin_fmaf(g[ii], Dv, sb) : __builtin_fmaf(g[ii], Dv, dti * sb);
-            float ddt = __builtin_fmaf(dd, kLn2, xv[i] * ((MODE & kExactZoh) ? sa : sb));
-            if (MODE & 1) ddt *= sg[i];
-            accT += ddt;
-            accD = __builtin_fmaf(g[ii], xv[i], accD);
-            if (dvalid) {
-              st(xo, (uint32_t)i * row_bytes, dxv);
-              st(po, (uint32_t)i * row_bytes, ddt);
+            if constexpr (kPart) {
+              if (dvalid) {
+                add_part(1, t0 + i, (MODE & kExactZoh) ? sb : dti * sb);
+                add_part(2, t0 + i, __builtin_fmaf(dd, kLn2, xv[i] * ((MODE & kExactZoh) ? sa : sb)));
+              }
+            } else {
+              const float dxv =
+                  (MODE & kExactZoh) ? __builtin_fmaf(g[ii], Dv, sb) : __builtin_fmaf(g[ii], Dv, dti * sb);
+              float ddt = __builtin_fmaf(dd, kLn2, xv[i] * ((MODE & kExactZoh) ? sa : sb));
+              if (MODE & 1) ddt *= sg[i];
+              accT += ddt;
+              accD = __builtin_fmaf(g[ii], xv[i], accD);
+              if (dvalid) {
+                st(xo, (uint32_t)i * row_bytes, dxv);
+                st(po, (uint32_t)i * row_bytes, ddt);
+              }
             }
           }
         }
@@ -617,13 +649,15 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
   if (dvalid) {
     if (dh0 != nullptr && chunk == 0) {
 #pragma unroll
-      for (int n = 0; n < N; ++n) dh0[(b * DI + d) * N + n] = lam[n];
+      for (int n = 0; n < N; ++n) dh0[(b * DI + d) * NF + n_off + n] = lam[n];
     }
     const int64_t row = (int64_t)chunk * dm.batch + b;
 #pragma unroll
-    for (int n = 0; n < N; ++n) part_a[(row * DI + d) * N + n] = gA[n];
-    part_d[row * DI + d] = accD;
-    part_t[row * DI + d] = accT;
+    for (int n = 0; n < N; ++n) part_a[(row * DI + d) * NF + n_off + n] = gA[n];
+    if (!kPart) {
+      part_d[row * DI + d] = accD;
+      part_t[row * DI + d] = accT;
+    }
   }
 }
 
@@ -724,7 +758,7 @@ hipError_t launch_bwd_t(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPla
     const float* lam_in = nullptr;
     if (nch > 1) {
       e = launch(k_bwd_lam_summary<T, N, MODE>, dim3((unsigned)(p.batch * (nch - 1) * tiles)), dim3(64), 0,
-                 p.stream, dl, p.A, Cm, zz, dyy, p.dt_bias, ws.lP, ws.lS, dm);
+                 p.stream, dl, p.A, Cm, zz, dyy, p.dt_bias, ws.lP, ws.lS, dm, 0);
       if (e != hipSuccess) return e;
       e = launch(k_bwd_lam_carry, dim3((unsigned)((states + 255) / 256)), dim3(256), 0, p.stream, p.dh_last, ws.lP,
                  ws.lS, ws.lIn, states, (int64_t)nch);
@@ -733,7 +767,7 @@ hipError_t launch_bwd_t(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPla
     }
     e = launch(k_bwd_sweep<T, N, MODE>, dim3(waves * nch), dim3(64), 0, p.stream, x, dl, p.A, Bm, Cm, p.D, zz, dyy,
                p.dh_last, p.dt_bias, ck, static_cast<T*>(p.dx), static_cast<T*>(p.ddelta), static_cast<T*>(p.dz),
-               p.dh0, ws.part_bc, ws.part_a, ws.part_d, ws.part_t, lam_in, dm);
+               p.dh0, ws.part_bc, ws.part_a, ws.part_d, ws.part_t, lam_in, dm, 0, (float*)nullptr);
     if (e != hipSuccess) return e;
   }
   const int64_t rows = p.batch * p.seqlen;
@@ -753,6 +787,136 @@ hipError_t launch_bwd_t(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPla
   return hipSuccess;
 }
 
+// Per-element gradients of a state-group backward (NF > 16): the groups'
+// fp32 sums in part_el plus the skip and gate terms, one thread per (b, d)
+// walking the sequence (a wave reads and writes whole rows).  Also the
+// per-row partials of dD (sum g x) and d_dt_bias (sum of the step gradient
+// through softplus' derivative), in row c = 0 of the [chunk][batch] layout
+// that k_bwd_reduce_params sums; rows of later chunks are zeroed.
+template <typename T, int MODE>
+__global__ void __launch_bounds__(256)
+    k_bwd_finalize(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ D,
+                   const T* __restrict__ z, const T* __restrict__ dy, const float* __restrict__ dt_bias,
+                   const float* __restrict__ part_el, T* __restrict__ dx, T* __restrict__ ddelta, T* __restrict__ dz,
+                   float* __restrict__ part_d, float* __restrict__ part_t, int64_t batch, int64_t seqlen,
+                   int64_t d_inner, int32_t n_chunks) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= batch * d_inner) return;
+  const int64_t b = i / d_inner, d = i - b * d_inner;
+  const float Dv = D != nullptr ? D[d] : 0.f;
+  const float dtb = (MODE & 1) ? dt_bias[d] : 0.f;
+  const int64_t plane = batch * seqlen * d_inner;
+  float accD = 0.f, accT = 0.f;
+  for (int64_t t = 0; t < seqlen; ++t) {
+    const int64_t o = (b * seqlen + t) * d_inner + d;
+    const float xv = io_to_f32(x[o]);
+    const float dyv = io_to_f32(dy[o]);
+    float g = dyv;
+    if (z != nullptr) {
+      const float zv = io_to_f32(z[o]);
+      const float sz = sigmoid(zv);
+      g = dyv * zv * sz;
+      const float ypre = __builtin_fmaf(Dv, xv, part_el[o]);
+      dz[o] = to_io<T>(ypre * (dyv * sz * __builtin_fmaf(zv, 1.f - sz, 1.f)));
+    }
+    dx[o] = to_io<T>(__builtin_fmaf(g, Dv, part_el[plane + o]));
+    float ddt = part_el[2 * plane + o];
+    if (MODE & 1) ddt *= sigmoid(io_to_f32(delta[o]) + dtb);
+    ddelta[o] = to_io<T>(ddt);
+    accT += ddt;
+    accD = __builtin_fmaf(g, xv, accD);
+  }
+  part_d[b * d_inner + d] = accD;
+  part_t[b * d_inner + d] = accT;
+  for (int c = 1; c < n_chunks; ++c) {
+    part_d[((int64_t)c * batch + b) * d_inner + d] = 0.f;
+    part_t[((int64_t)c * batch + b) * d_inner + d] = 0.f;
+  }
+}
+
+// Backward for NF = 32, 64 or 128 states: the 16-state sweep once per group
+// of 16 states (see k_bwd_sweep), then k_bwd_finalize.  Checkpoints come
+// from the forward sweep's state-only mode with NF / 16 waves per tile.
+template <typename T, int NF, int MODE>
+hipError_t launch_bwd_groups(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPlan& pl) {
+  constexpr int NG = 16;
+  constexpr int G = NF / NG;
+  const int64_t tiles = (p.d_inner + 63) / 64;
+  const int nch = (int)pl.n_chunks;
+  const BwdDims dm{p.batch, p.seqlen, p.d_inner, (int32_t)tiles, (int32_t)((p.seqlen + kBB - 1) / kBB), nch,
+                   (int32_t)(pl.chunk_len / kBB)};
+  const T* x = static_cast<const T*>(p.x);
+  const T* dl = static_cast<const T*>(p.delta);
+  const T* Bm = static_cast<const T*>(p.B);
+  const T* Cm = static_cast<const T*>(p.C);
+  const T* zz = static_cast<const T*>(p.z);
+  const T* dyy = static_cast<const T*>(p.dy);
+  const int64_t states = p.batch * p.d_inner * NF;
+  hipError_t e;
+  const unsigned waves = (unsigned)(p.batch * tiles);
+  if (waves > 0) {
+    const float* ck = p.ckpt;
+    if (ck == nullptr && dm.nblk > 0) {
+      const float* h_entry = nullptr;
+      if (nch > 1) {
+        SweepDims sd{p.batch, p.seqlen, p.d_inner, pl.chunk_len, (int32_t)tiles, nch - 1, nch, 0, nullptr};
+        e = launch(k_scan_sweep<T, NF, NG, true, MODE>, dim3((unsigned)(p.batch * (nch - 1) * tiles)), dim3(64 * G),
+                   0, p.stream, x, dl, p.A, Bm, Cm, (const float*)nullptr, zz, (const float*)nullptr, (T*)nullptr,
+                   (float*)nullptr, ws.fP, ws.fS, p.dt_bias, sd);
+        if (e != hipSuccess) return e;
+        e = launch_chunk_carry(p.h0, ws.fP, ws.fS, ws.fH, states, nch, p.stream);
+        if (e != hipSuccess) return e;
+        h_entry = ws.fH;
+      }
+      SweepDims cd{p.batch, p.seqlen, p.d_inner, pl.chunk_len, (int32_t)tiles, nch, nch, h_entry != nullptr ? 1 : 0,
+                   ws.ckpt};
+      e = launch(k_scan_sweep<T, NF, NG, true, MODE>, dim3(waves * nch), dim3(64 * G), 0, p.stream, x, dl, p.A, Bm,
+                 Cm, (const float*)nullptr, zz, h_entry != nullptr ? h_entry : p.h0, (T*)nullptr, (float*)nullptr,
+                 (float*)nullptr, (float*)nullptr, p.dt_bias, cd);
+      if (e != hipSuccess) return e;
+      ck = ws.ckpt;
+    }
+    const float* lam_in = nullptr;
+    if (nch > 1) {
+      for (int gi = 0; gi < G; ++gi) {
+        e = launch(k_bwd_lam_summary<T, NG, MODE, NF>, dim3((unsigned)(p.batch * (nch - 1) * tiles)), dim3(64), 0,
+                   p.stream, dl, p.A, Cm, zz, dyy, p.dt_bias, ws.lP, ws.lS, dm, NG * gi);
+        if (e != hipSuccess) return e;
+      }
+      e = launch(k_bwd_lam_carry, dim3((unsigned)((states + 255) / 256)), dim3(256), 0, p.stream, p.dh_last, ws.lP,
+                 ws.lS, ws.lIn, states, (int64_t)nch);
+      if (e != hipSuccess) return e;
+      lam_in = ws.lIn;
+    }
+    for (int gi = 0; gi < G; ++gi) {
+      e = launch(k_bwd_sweep<T, NG, MODE, NF>, dim3(waves * nch), dim3(64), 0, p.stream, x, dl, p.A, Bm, Cm, p.D, zz,
+                 dyy, p.dh_last, p.dt_bias, ck, static_cast<T*>(p.dx), static_cast<T*>(p.ddelta),
+                 static_cast<T*>(p.dz), p.dh0, ws.part_bc, ws.part_a, ws.part_d, ws.part_t, lam_in, dm, NG * gi,
+                 ws.part_el);
+      if (e != hipSuccess) return e;
+    }
+    const int64_t rows_bd = p.batch * p.d_inner;
+    e = launch(k_bwd_finalize<T, MODE>, dim3((unsigned)((rows_bd + 255) / 256)), dim3(256), 0, p.stream, x, dl, p.D,
+               zz, dyy, p.dt_bias, (const float*)ws.part_el, static_cast<T*>(p.dx), static_cast<T*>(p.ddelta),
+               static_cast<T*>(p.dz), ws.part_d, ws.part_t, p.batch, p.seqlen, p.d_inner, (int32_t)nch);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t rows = p.batch * p.seqlen;
+  if (rows > 0) {
+    const int64_t total = rows * 2 * NF;
+    e = launch(k_bwd_reduce_bc, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, p.stream, ws.part_bc, p.dB,
+               p.dC, rows, (int32_t)NF, (int32_t)tiles);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t na = p.d_inner * NF;
+  if (na > 0) {
+    e = launch(k_bwd_reduce_params, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, p.stream, ws.part_a,
+               ws.part_d, ws.part_t, p.dA, p.dD, p.d_dt_bias, p.batch * nch, p.d_inner, (int32_t)NF);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <typename T, int MODE>
 hipError_t launch_bwd_n(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPlan& pl) {
   switch (p.d_state) {
@@ -760,6 +924,9 @@ hipError_t launch_bwd_n(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPla
     case 4: return launch_bwd_t<T, 4, MODE>(p, ws, pl);
     case 8: return launch_bwd_t<T, 8, MODE>(p, ws, pl);
     case 16: return launch_bwd_t<T, 16, MODE>(p, ws, pl);
+    case 32: return launch_bwd_groups<T, 32, MODE>(p, ws, pl);
+    case 64: return launch_bwd_groups<T, 64, MODE>(p, ws, pl);
+    case 128: return launch_bwd_groups<T, 128, MODE>(p, ws, pl);
     default: return hipErrorInvalidValue;
   }
 }
@@ -808,6 +975,8 @@ BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, in
   // Forward chunk summaries and entry states: only to compute checkpoints.
   const int64_t n_fsum = ckpt_given ? 0 : n_sum;
   const int64_t n_fent = ckpt_given ? 0 : n_ent;
+  // Per-element sums of the state groups (more than 16 states).
+  const int64_t n_el = d_state > 16 ? up(3 * batch * seqlen * d_inner) : 0;
   BwdWorkspace ws{};
   if (base != nullptr) {
     ws.ckpt = ckpt_given ? nullptr : base;
@@ -822,8 +991,10 @@ BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, in
     ws.lP = f + 2 * n_fsum + n_fent;
     ws.lS = ws.lP + n_sum;
     ws.lIn = ws.lS + n_sum;
+    ws.part_el = n_el > 0 ? ws.lIn + n_ent : nullptr;
   }
-  if (total_floats != nullptr) *total_floats = n_ck + n_bc + n_a + 2 * n_d + 2 * n_fsum + n_fent + 2 * n_sum + n_ent;
+  if (total_floats != nullptr)
+    *total_floats = n_ck + n_bc + n_a + 2 * n_d + 2 * n_fsum + n_fent + 2 * n_sum + n_ent + n_el;
   return ws;
 }
 

@@ -140,7 +140,9 @@ BwdPlan bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner);
 //   part_d, part_t [c][batch][d_inner]                 per-(chunk, row) dD, d_dt_bias
 //   when c > 1: forward chunk summaries fP, fS [c-1][S] and entry states fH
 //   [c][S]; adjoint chunk summaries lP, lS [c-1][S] and incoming adjoints
-//   lIn [c][S].
+//   lIn [c][S];
+//   when d_state > 16: part_el [3][batch][seqlen][d_inner], the state groups'
+//   per-element sums.
 struct BwdWorkspace {
   float* ckpt;
   float* part_bc;
@@ -153,6 +155,7 @@ struct BwdWorkspace {
   float* lP;
   float* lS;
   float* lIn;
+  float* part_el;  // more than 16 states: per-element sums of the state groups, [3][batch][seqlen][d_inner]
 };
 BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                                   const BwdPlan& plan, bool ckpt_given, int64_t* total_floats);

@@ -208,7 +208,11 @@ def test_bwd_workspace_size(lib):
     tiles, nblk = 3, 3
     want = (up(b * nblk * N * d) + up(tiles * b * L * 2 * N) + up(b * d * N) + 2 * up(b * d)) * 4
     assert lib.ssm_scan_bwd_workspace_size(b, L, d, N) == want
-    assert lib.ssm_scan_bwd_workspace_size(b, L, d, 32) == ctypes.c_size_t(-1).value
+    assert lib.ssm_scan_bwd_workspace_size(b, L, d, 256) == ctypes.c_size_t(-1).value
+    assert lib.ssm_scan_bwd_workspace_size(b, L, d, 24) == ctypes.c_size_t(-1).value
+    # Above 16 states: the state groups' per-element sums, 3 floats per element.
+    want32 = (up(b * nblk * 32 * d) + up(tiles * b * L * 2 * 32) + up(b * d * 32) + 2 * up(b * d) + up(3 * b * L * d)) * 4
+    assert lib.ssm_scan_bwd_workspace_size(b, L, d, 32) == want32
     assert lib.ssm_scan_bwd_workspace_size(-1, L, d, N) == ctypes.c_size_t(-1).value
     assert bd.scan_bwd_workspace_size(0, 0, 0, 16) == 0
     # With the forward call's checkpoints the checkpoint section is left out.
@@ -245,11 +249,12 @@ def test_bwd_argument_errors(lib):
     zoh = bd.SSM_FLAG_EXACT_ZOH
     assert _bwd(lib, flags=zoh, dx=None) == bd.SSM_ERR_NULL_ARG
     assert _bwd(lib, flags=zoh | sp, dt_bias=P0 + 8 * MB) == bd.SSM_ERR_NULL_ARG
-    # Unsupported: unknown flags, d_state outside {2,4,8,16}, dtype.
+    # Unsupported: unknown flags, d_state outside {2,4,...,128}, dtype.
     assert _bwd(lib, flags=0x40) == bd.SSM_ERR_UNSUPPORTED
     assert _bwd(lib, flags=zoh | 0x40) == bd.SSM_ERR_UNSUPPORTED
-    assert _bwd(lib, N=32) == bd.SSM_ERR_UNSUPPORTED
+    assert _bwd(lib, N=256) == bd.SSM_ERR_UNSUPPORTED
     assert _bwd(lib, N=3) == bd.SSM_ERR_UNSUPPORTED
+    assert _bwd(lib, N=64, ws_bytes=lib.ssm_scan_bwd_workspace_size(2, 4, 8, 64) - 4) == bd.SSM_ERR_WORKSPACE
     assert _bwd(lib, dtype=5) == bd.SSM_ERR_UNSUPPORTED
     assert _bwd(lib, batch=-1) == bd.SSM_ERR_BAD_DIM
     assert _bwd(lib, batch=1, L=(1 << 31) - 100, d=1, ws_bytes=0) == bd.SSM_ERR_BAD_DIM

@@ -375,3 +375,41 @@ def test_bwd_max_d_inner(lib):
     del gr, d
     torch.cuda.empty_cache()
     _compare(got, ref, F32_GATE, keys=list(got), label="bwd max d_inner")
+
+
+@pytest.mark.parametrize("d_state", [32, 64, 128])
+@pytest.mark.parametrize("dtype,flags", [("f32", 0), ("bf16", 0), ("f32", SP | ZOH), ("bf16", SP)])
+def test_bwd_large_d_state(lib, d_state, dtype, flags):
+    """More than 16 states: one 16-state sweep per group of states, the
+    groups' per-element sums combined afterwards.  Ragged steps and channels,
+    every optional input, per-channel A and D."""
+    sp, zoh = bool(flags & SP), bool(flags & ZOH)
+    inp = inputs.make_scan_inputs(2, 37, 100, d_state, dtype, 1900 + d_state + flags, nonzero_h0=True, raw_delta=sp,
+                                  params="random")
+    gr = inputs.make_scan_grads(2, 37, 100, d_state, dtype, 1900 + d_state)
+    print("case bwd large N", d_state, dtype, flags, flush=True)
+    _compare(_gpu(inp, gr, softplus=sp, zoh=zoh), _ref(inp, gr, softplus=sp, zoh=zoh), _gate(dtype),
+             label="bwd N=%d %s flags %d" % (d_state, dtype, flags))
+
+
+@pytest.mark.parametrize("fwd_ckpt", [False, True])
+def test_bwd_large_d_state_sequence_chunks(lib, fwd_ckpt):
+    """64 states, a long sequence with few channels: the backward cuts it into
+    chunks (adjoint summaries per state group, forward summaries with four
+    waves per tile unless the forward call's checkpoints are passed)."""
+    import torch
+    from gpu_util import to_dev, to_host_f64
+    from selective_state_space_84_amd import binding
+    batch, L, dI, N = 2, 1013, 70, 64
+    inp = inputs.make_scan_inputs(batch, L, dI, N, "f32", 1950 + fwd_ckpt, nonzero_h0=True, params="random")
+    gr = inputs.make_scan_grads(batch, L, dI, N, "f32", 1950)
+    print("case bwd large N chunks", fwd_ckpt, flush=True)
+    d = {k: to_dev(inp.get(k)) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0")}
+    ck = None
+    if fwd_ckpt:
+        ck = torch.empty((binding.scan_ckpt_bytes(batch, L, dI, N) // 4,), device="cuda:0")
+        binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], ckpt_out=ck)
+    g = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
+                             dy=to_dev(gr["dy"]), dh_last=to_dev(gr["dh_last"]), ckpt=ck)
+    torch.cuda.synchronize()
+    _compare({k: to_host_f64(v) for k, v in g.items()}, _ref(inp, gr), F32_GATE, label="N=64 chunks ckpt=%d" % fwd_ckpt)
