@@ -125,6 +125,11 @@ def _ulps(got, ref):
 
 def _emulate(inp, softplus, zoh=False, ideal_softplus=False):
     """The sweep's per-step arithmetic in float32 (correctly rounded primitives)."""
+    with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+        return _emulate_steps(inp, softplus, zoh, ideal_softplus)
+
+
+def _emulate_steps(inp, softplus, zoh, ideal_softplus):
     x, dl, A, Bm, Cm, Dv, z, h0, dtb = (inp[k] for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "dt_bias"))
     Al2 = _mul(A, L2E)
     with np.errstate(divide="ignore"):
