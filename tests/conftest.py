@@ -41,6 +41,10 @@ def oracle_mod():
 def lib():
     """The HIP library, built in-tree when nothing is built yet."""
     from selective_state_space_84_amd import binding, build_lib
+    other = os.environ.get("SSM_TEST_LIBRARY")
+    if other:  # a differently built copy of the same sources (the sanitizer build)
+        binding._lib = binding.load_library(other)
+        return binding._lib
     if not os.path.exists(binding.LIB_PATH):
         build_lib.build()
     return binding.load_library()
