@@ -70,6 +70,7 @@ constexpr int kQ = 32;           // chunk length
 constexpr int kHP = 64;          // channels per head
 constexpr int kSX = kHP + 16;    // x tile row stride (bf16): 40 dwords, transposing reads conflict-free
 constexpr int kSW = kQ + 8;      // score tile row stride: 20 dwords, 16-byte reads conflict-free
+constexpr int kSZ = kHP + 8;     // gate-in / output-out tile row stride: 36 dwords
 
 struct SsdDims {
   int64_t batch, seqlen;
@@ -148,6 +149,8 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   __shared__ __align__(16) uint16_t sC[2][kQ * SC];
   __shared__ __align__(16) uint16_t sW[2][kQ * kSW];  // masked scores [k][i], hi and lo planes
   __shared__ __align__(16) float sv[4][4][kQ];         // per wave: l (log2 units), dt, w, exp(l)
+  __shared__ __align__(16) uint16_t sZY[kQ * kSZ];    // gate inputs in, outputs out, row-major
+  __shared__ uint16_t sDt[kQ];                        // the chunk's raw steps
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,7 +196,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   const int bq = tid % NQ, tq = tid / NQ;  // B: states 4 bq .. +3 of steps 4 tq .. +3
   u16x8 rx, rc[PB];
   u32x2 rb[4];
-  u32x2 rz[2];
+  u16x8 rz = {};
   uint16_t rdt = 0;
   // The next chunk's rows are requested in two groups, B and C after the
   // first barrier and x, dt and the gate inputs after the second, so that
@@ -205,12 +208,12 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     const gchar* xb = uniform_ptr(x + ((b * L + t0) * dm.nheads + h) * kHP);
     rx = gldr<u16x8>(xb, __umul24((uint32_t)min(sx_t, last), rowb) + sx_c * 2);
     const gchar* db = uniform_ptr(dt + (b * L + t0) * dm.nheads + h);
-    rdt = gldr<uint16_t>(db, __umul24((uint32_t)min(lane, last), (uint32_t)dm.nheads * 2));
+    // The steps: one wave loads them (lane = step) and shares them through LDS.
+    if (w == 0) rdt = gldr<uint16_t>(db, __umul24((uint32_t)min(lane, last), (uint32_t)dm.nheads * 2));
     if (kGate) {
-      // Gate inputs in the Y^T layout: rows 16 kt + r16, channels 16w + 4q4 .. +3.
-      const gchar* zb = uniform_ptr(z + ((b * L + t0) * dm.nheads + h) * kHP + 16 * w);
-      rz[0] = gldr<u32x2>(zb, __umul24((uint32_t)min(r16, last), rowb) + 8 * q4);
-      rz[1] = gldr<u32x2>(zb, __umul24((uint32_t)min(16 + r16, last), rowb) + 8 * q4);
+      // Gate inputs in whole rows, like x: they pass through LDS into the Y^T layout.
+      const gchar* zb = uniform_ptr(z + ((b * L + t0) * dm.nheads + h) * kHP);
+      rz = gldr<u16x8>(zb, __umul24((uint32_t)min(sx_t, last), rowb) + sx_c * 2);
     }
   };
   auto fetch = [&](int64_t c) {
@@ -232,6 +235,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   // x, C and the row copy of B, before the chunk's first barrier.
   auto stage = [&](int buf) {
     *reinterpret_cast<u16x8*>(&sX[sx_t * kSX + sx_c]) = rx;
+    if (w == 0 && lane < kQ) sDt[lane] = rdt;
     if (BT == 256 || w < BT / 64) {
       const int s0 = (4 * bq) & ~31, o = (4 * bq) & 31;
 #pragma unroll
@@ -269,9 +273,19 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     const int64_t t0 = c * kQ;
     const int nt_ = (int)min((int64_t)kQ, L - t0);
     stage(buf);
-    const uint16_t dcur = rdt;
-    const u32x2 zv[2] = {rz[0], rz[1]};
     __syncthreads();
+    // The previous chunk's outputs leave in whole 128-byte rows, and this
+    // chunk's gate inputs take their place: every thread reads, stores and
+    // refills the same 16 bytes of the tile (only the last chunk can be
+    // short, and it is stored after the loop).
+    {
+      uint16_t* slot = &sZY[sx_t * kSZ + sx_c];
+      if (c > 0) {
+        gchar* yp = uniform_ptr(y + ((b * L + t0 - kQ) * dm.nheads + h) * kHP);
+        gstr<u16x8>(yp, __umul24((uint32_t)sx_t, rowb) + sx_c * 2, *reinterpret_cast<const u16x8*>(slot));
+      }
+      if (kGate) *reinterpret_cast<u16x8*>(slot) = rz;
+    }
     stage_bt();
     if (c + 1 < nchunks) fetch(c + 1);
 
@@ -280,7 +294,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     {
       float d = 0.f;
       if (lane < nt_) {
-        d = lo_f32(dcur);
+        d = lo_f32(sDt[lane]);
         if (MODE & 1) d = softplus(d, dtb);
       }
       const float l = scan32(d * Al2);
@@ -343,7 +357,6 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
       hhi[kk] = as_u16x8(vh);
       hlo[kk] = as_u16x8(vl);
     }
-    gchar* yb = uniform_ptr(y + ((b * L + t0) * dm.nheads + h) * kHP + 16 * w);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int k = 16 * kt + r16;
@@ -363,15 +376,16 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
       float v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = accY[j] + ek * accO[j];
+      // This lane's 8 bytes of the tile: its gate inputs, then its outputs.
+      u32x2* const yz = reinterpret_cast<u32x2*>(&sZY[k * kSZ + 16 * w + 4 * q4]);
       if (kGate) {
-        const u32x2 zz = zv[kt];
+        const u32x2 zz = *yz;
         v[0] *= silu(lo_f32(zz.x));
         v[1] *= silu(hi_f32(zz.x));
         v[2] *= silu(lo_f32(zz.y));
         v[3] *= silu(hi_f32(zz.y));
       }
-      // Row k of this wave's channels 16w + 4q4 .. +3 (8 bytes).
-      if (k < nt_) gstr<u32x2>(yb, __umul24((uint32_t)k, rowb) + 8 * q4, u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
+      *yz = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
     }
 
     // 5. State: H = exp(l_Q) H + B^T (w o X).
@@ -399,6 +413,16 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
       acc = mma(bt, xwh, acc);
       acc = mma(bt, xwl, acc);
       accH[nt] = acc;
+    }
+  }
+
+  // The last chunk's outputs (its first nt rows).
+  __syncthreads();
+  if (nchunks > 0) {
+    const int64_t t0 = (nchunks - 1) * kQ;
+    if (sx_t < L - t0) {
+      gchar* yp = uniform_ptr(y + ((b * L + t0) * dm.nheads + h) * kHP);
+      gstr<u16x8>(yp, __umul24((uint32_t)sx_t, rowb) + sx_c * 2, *reinterpret_cast<const u16x8*>(&sZY[sx_t * kSZ + sx_c]));
     }
   }
 
