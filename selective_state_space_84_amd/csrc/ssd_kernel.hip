@@ -148,9 +148,8 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   __shared__ __align__(16) uint16_t sBt[NQ * GT];      // B^T: (n, t) at (n / 4) GT + (n % 4) kQ + t
   __shared__ __align__(16) uint16_t sC[2][kQ * SC];
   __shared__ __align__(16) uint16_t sW[2][kQ * kSW];  // masked scores [k][i], hi and lo planes
-  __shared__ __align__(16) float sv[4][4][kQ];         // per wave: l (log2 units), dt, w, exp(l)
+  __shared__ __align__(16) float sv[2][4][kQ];         // l (log2 units), dt, w, exp(l); double-buffered
   __shared__ __align__(16) uint16_t sZY[kQ * kSZ];    // gate inputs in, outputs out, row-major
-  __shared__ uint16_t sDt[kQ];                        // the chunk's raw steps
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -168,10 +167,6 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   const float Al2 = A[h] * kLog2e;
   const float Dh = D != nullptr ? D[h] : 0.f;
   const float dtb = (MODE & 1) ? dt_bias[h] : 0.f;
-  float* const lv = &sv[w][0][0];
-  float* const dv = &sv[w][1][0];
-  float* const wv = &sv[w][2][0];
-  float* const ev = &sv[w][3][0];
 
   // State H[n][p] for p = 16w + r16: accH[nt][j] = H[16 nt + 4 q4 + j][p].
   f32x4 accH[NT];
@@ -208,8 +203,8 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     const gchar* xb = uniform_ptr(x + ((b * L + t0) * dm.nheads + h) * kHP);
     rx = gldr<u16x8>(xb, __umul24((uint32_t)min(sx_t, last), rowb) + sx_c * 2);
     const gchar* db = uniform_ptr(dt + (b * L + t0) * dm.nheads + h);
-    // The steps: one wave loads them (lane = step) and shares them through LDS.
-    if (w == 0) rdt = gldr<uint16_t>(db, __umul24((uint32_t)min(lane, last), (uint32_t)dm.nheads * 2));
+    // The steps (lane = step), for wave 3, which turns them into decay sums.
+    if (w == 3) rdt = gldr<uint16_t>(db, __umul24((uint32_t)min(lane, last), (uint32_t)dm.nheads * 2));
     if (kGate) {
       // Gate inputs in whole rows, like x: they pass through LDS into the Y^T layout.
       const gchar* zb = uniform_ptr(z + ((b * L + t0) * dm.nheads + h) * kHP);
@@ -235,7 +230,6 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   // x, C and the row copy of B, before the chunk's first barrier.
   auto stage = [&](int buf) {
     *reinterpret_cast<u16x8*>(&sX[sx_t * kSX + sx_c]) = rx;
-    if (w == 0 && lane < kQ) sDt[lane] = rdt;
     if (BT == 256 || w < BT / 64) {
       const int s0 = (4 * bq) & ~31, o = (4 * bq) & 31;
 #pragma unroll
@@ -266,12 +260,36 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     }
   };
 
+  // Steps and decay sums of chunk cc (lane = step) into sv[cc & 1], by wave 3
+  // (the one without a score tile), a chunk ahead of their use.  Steps past
+  // the end count as dt = 0: decay 1, no input.
+  auto decay_sums = [&](int64_t cc) {
+    const int ntc = (int)min((int64_t)kQ, L - cc * kQ);
+    float d = 0.f;
+    if (lane < ntc) {
+      d = lo_f32(rdt);
+      if (MODE & 1) d = softplus(d, dtb);
+    }
+    const float l = scan32(d * Al2);
+    const float lq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), kQ - 1));
+    if (lane < kQ) {
+      float* const sd = &sv[cc & 1][0][0];
+      sd[lane] = l;
+      sd[kQ + lane] = d;
+      sd[2 * kQ + lane] = hw_exp2(lq - l) * d;
+      sd[3 * kQ + lane] = hw_exp2(l);
+    }
+  };
+
   const int64_t nchunks = (L + kQ - 1) / kQ;
-  if (nchunks > 0) { fetch(0); fetch_xz(0); }
+  if (nchunks > 0) {
+    fetch(0);
+    fetch_xz(0);
+    if (w == 3) decay_sums(0);
+  }
   for (int64_t c = 0; c < nchunks; ++c) {
     const int buf = (int)(c & 1);
     const int64_t t0 = c * kQ;
-    const int nt_ = (int)min((int64_t)kQ, L - t0);
     stage(buf);
     __syncthreads();
     // The previous chunk's outputs leave in whole 128-byte rows, and this
@@ -289,24 +307,11 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     stage_bt();
     if (c + 1 < nchunks) fetch(c + 1);
 
-    // 1. Steps and decay sums (every wave for itself; lane = step).  Steps
-    //    past the end count as dt = 0: decay 1, no input.
-    {
-      float d = 0.f;
-      if (lane < nt_) {
-        d = lo_f32(sDt[lane]);
-        if (MODE & 1) d = softplus(d, dtb);
-      }
-      const float l = scan32(d * Al2);
-      const float lq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), kQ - 1));
-      if (lane < kQ) {
-        lv[lane] = l;
-        dv[lane] = d;
-        wv[lane] = hw_exp2(lq - l) * d;
-        ev[lane] = hw_exp2(l);
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // 1. This chunk's decay sums (written by wave 3 before the barrier).
+    const float* const lv = &sv[buf][0][0];
+    const float* const dv = lv + kQ;
+    const float* const wv = lv + 2 * kQ;
+    const float* const ev = lv + 3 * kQ;
     const float decay = hw_exp2(lv[kQ - 1]);
 
     // 2. Score tile (it, kt) = (0,0), (0,1), (1,1) for waves 0, 1, 2:
@@ -414,6 +419,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
       acc = mma(bt, xwl, acc);
       accH[nt] = acc;
     }
+    if (w == 3 && c + 1 < nchunks) decay_sums(c + 1);
   }
 
   // The last chunk's outputs (its first nt rows).
