@@ -210,8 +210,9 @@ int ssm_scan_fwd_ex(const void* x, const void* delta, const float* A, const void
  * the process ends.
  *   - Arguments, results and errors as for ssm_scan_fwd_ex (opts may be NULL).
  *   - With an automatic chunk length (opts NULL or chunk_len 0) the plan keeps
- *     as many chunks as the scratch holds ((3 n - 2) * batch * d_inner *
- *     d_state floats for n chunks), down to one unsplit sweep; results equal
+ *     as many chunks as the scratch holds (for n chunks, (2 n - 1) *
+ *     batch * d_inner * d_state floats of states plus (n - 1) * batch *
+ *     d_inner step sums rounded up to 64), down to one unsplit sweep; results equal
  *     ssm_scan_fwd_ex's up to fp32 rounding of the chunk carries.
  *   - An explicit chunk_len whose carries exceed the scratch returns
  *     SSM_ERR_WORKSPACE before anything is enqueued.

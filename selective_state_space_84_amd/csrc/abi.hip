@@ -121,11 +121,14 @@ int workspace_bytes_for(int64_t batch, int64_t d_inner, int64_t d_state, const P
   int64_t states;
   if (!mul3(batch, d_inner, d_state, &states)) return SSM_ERR_BAD_DIM;
   const int64_t nch = pl.n_chunks;
-  int64_t floats;
-  if (nch <= 1) {
-    floats = 0;
-  } else if (__builtin_mul_overflow(3 * nch - 2, states, &floats)) {
-    return SSM_ERR_BAD_DIM;
+  int64_t floats = 0;
+  if (nch > 1) {
+    // Step sums (one per row and chunk, rounded up to 64) and 2n - 1 state sets.
+    int64_t sets, sums;
+    if (__builtin_mul_overflow(2 * nch - 1, states, &sets) || __builtin_mul_overflow(nch - 1, batch * d_inner, &sums) ||
+        __builtin_add_overflow(sets, sums + 63, &floats))
+      return SSM_ERR_BAD_DIM;
+    floats = sets + ssm::scan_stepsum_floats(nch, batch * d_inner);
   }
   int64_t bytes;
   if (__builtin_mul_overflow(floats, (int64_t)sizeof(float), &bytes)) return SSM_ERR_BAD_DIM;
@@ -133,7 +136,7 @@ int workspace_bytes_for(int64_t batch, int64_t d_inner, int64_t d_state, const P
   return SSM_OK;
 }
 
-// Device scratch of ssm_scan_fwd_noalloc: the chunk carries (decay products,
+// Device scratch of ssm_scan_fwd_noalloc: the chunk carries (step sums,
 // zero-start end states, entry states) of a split sequence live here instead
 // of in a caller workspace.  Each device holds its own copy from the first
 // call on it until the process ends.  In host code `scratch` names a host-side
@@ -163,12 +166,16 @@ int device_scratch(void** out) {
 }
 
 // With no caller workspace, the automatic plan keeps as many sequence chunks
-// as the scratch holds: n chunks need (3n - 2) * batch * d_inner * d_state
-// floats.  Fewer than two fitting chunks means one unsplit sweep.
+// as the scratch holds: n chunks need up64((n - 1) * R) + (2n - 1) * S floats
+// (R = batch * d_inner rows, S = R * d_state states).  Fewer than two fitting
+// chunks means one unsplit sweep.
 void cap_plan_to_scratch(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, Plan* pl) {
-  const int64_t states = batch * d_inner * d_state;
+  const int64_t rows = batch * d_inner, states = rows * d_state;
   if (pl->n_chunks <= 1 || states <= 0) return;
-  const int64_t n_max = ((int64_t)(kScratchBytes / sizeof(float)) / states + 2) / 3;
+  const int64_t cap = (int64_t)(kScratchBytes / sizeof(float));
+  auto fits = [&](int64_t n) { return ssm::scan_stepsum_floats(n, rows) + (2 * n - 1) * states <= cap; };
+  int64_t n_max = (cap - 64 + rows + states) / (rows + 2 * states);
+  while (n_max > 1 && !fits(n_max)) --n_max;
   if (pl->n_chunks <= n_max) return;
   if (n_max < 2) {
     pl->chunk_len = seqlen;

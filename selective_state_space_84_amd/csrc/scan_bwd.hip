@@ -739,9 +739,10 @@ hipError_t launch_bwd_t(const BwdLaunch& p, const BwdWorkspace& ws, const BwdPla
         SweepDims sd{p.batch, p.seqlen, p.d_inner, pl.chunk_len, (int32_t)tiles, nch - 1, nch, 0, nullptr};
         e = launch(k_scan_sweep<T, N, N, true, MODE>, dim3((unsigned)(p.batch * (nch - 1) * tiles)), dim3(64), 0,
                    p.stream, x, dl, p.A, Bm, Cm, (const float*)nullptr, zz, (const float*)nullptr, (T*)nullptr,
-                   (float*)nullptr, ws.fP, ws.fS, p.dt_bias, sd);
+                   (float*)nullptr, ws.fT, ws.fS, p.dt_bias, sd);
         if (e != hipSuccess) return e;
-        e = launch_chunk_carry(p.h0, ws.fP, ws.fS, ws.fH, states, nch, p.stream);
+        e = launch_chunk_carry(p.h0, p.A, (MODE & kLinearA) != 0, ws.fT, ws.fS, ws.fH, p.batch * p.d_inner, N,
+                               p.d_inner, nch, p.stream);
         if (e != hipSuccess) return e;
         h_entry = ws.fH;
       }
@@ -862,9 +863,10 @@ hipError_t launch_bwd_groups(const BwdLaunch& p, const BwdWorkspace& ws, const B
         SweepDims sd{p.batch, p.seqlen, p.d_inner, pl.chunk_len, (int32_t)tiles, nch - 1, nch, 0, nullptr};
         e = launch(k_scan_sweep<T, NF, NG, true, MODE>, dim3((unsigned)(p.batch * (nch - 1) * tiles)), dim3(64 * G),
                    0, p.stream, x, dl, p.A, Bm, Cm, (const float*)nullptr, zz, (const float*)nullptr, (T*)nullptr,
-                   (float*)nullptr, ws.fP, ws.fS, p.dt_bias, sd);
+                   (float*)nullptr, ws.fT, ws.fS, p.dt_bias, sd);
         if (e != hipSuccess) return e;
-        e = launch_chunk_carry(p.h0, ws.fP, ws.fS, ws.fH, states, nch, p.stream);
+        e = launch_chunk_carry(p.h0, p.A, (MODE & kLinearA) != 0, ws.fT, ws.fS, ws.fH, p.batch * p.d_inner, NF,
+                               p.d_inner, nch, p.stream);
         if (e != hipSuccess) return e;
         h_entry = ws.fH;
       }
@@ -972,7 +974,9 @@ BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, in
   const int64_t n_d = up(nch * batch * d_inner);
   const int64_t n_sum = nch > 1 ? up((nch - 1) * states) : 0;
   const int64_t n_ent = nch > 1 ? up(nch * states) : 0;
-  // Forward chunk summaries and entry states: only to compute checkpoints.
+  // Forward chunk summaries (step sums, end states) and entry states: only to
+  // compute checkpoints.
+  const int64_t n_ftsum = ckpt_given ? 0 : scan_stepsum_floats(nch, batch * d_inner);
   const int64_t n_fsum = ckpt_given ? 0 : n_sum;
   const int64_t n_fent = ckpt_given ? 0 : n_ent;
   // Per-element sums of the state groups (more than 16 states).
@@ -985,16 +989,16 @@ BwdWorkspace bwd_workspace_layout(float* base, int64_t batch, int64_t seqlen, in
     ws.part_d = ws.part_a + n_a;
     ws.part_t = ws.part_d + n_d;
     float* f = ws.part_t + n_d;
-    ws.fP = ckpt_given ? nullptr : f;
-    ws.fS = ckpt_given ? nullptr : f + n_fsum;
-    ws.fH = ckpt_given ? nullptr : f + 2 * n_fsum;
-    ws.lP = f + 2 * n_fsum + n_fent;
+    ws.fT = ckpt_given ? nullptr : f;
+    ws.fS = ckpt_given ? nullptr : f + n_ftsum;
+    ws.fH = ckpt_given ? nullptr : f + n_ftsum + n_fsum;
+    ws.lP = f + n_ftsum + n_fsum + n_fent;
     ws.lS = ws.lP + n_sum;
     ws.lIn = ws.lS + n_sum;
     ws.part_el = n_el > 0 ? ws.lIn + n_ent : nullptr;
   }
   if (total_floats != nullptr)
-    *total_floats = n_ck + n_bc + n_a + 2 * n_d + 2 * n_fsum + n_fent + 2 * n_sum + n_ent + n_el;
+    *total_floats = n_ck + n_bc + n_a + 2 * n_d + n_ftsum + n_fsum + n_fent + 2 * n_sum + n_ent + n_el;
   return ws;
 }
 

@@ -145,18 +145,18 @@ struct SweepDims {
 
 // One sweep over a (batch row, chunk, 64-channel tile).  N = d_state, NS =
 // states per wave, G = N / NS waves per workgroup.
-// SUMMARY = true: no readout.  As the chunk summary (h_init and sumP null:
-// state from zero) it writes P = exp(A * sum(delta)) and the end state S of
-// chunk c into sumP / sumS; given h_init and checkpoints instead (and null
-// sumP / sumS) it is the state-only sweep that writes the checkpoints for
-// the backward pass.
+// SUMMARY = true: no readout.  As the chunk summary (h_init null: state from
+// zero) it writes the sum of chunk c's steps T and its end state S into
+// sumT / sumS (the chunk's decay product is exp(A * T)); given h_init and
+// checkpoints instead (and null sumT / sumS) it is the state-only sweep that
+// writes the checkpoints for the backward pass.
 // SUMMARY = false: full sweep with readout, gate, y store and h_last.
 template <typename T, int N, int NS, bool SUMMARY, int MODE>
 __global__ void __launch_bounds__(64 * (N / NS))
     k_scan_sweep(const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
                  const T* __restrict__ B, const T* __restrict__ C, const float* __restrict__ D,
                  const T* __restrict__ z, const float* __restrict__ h_init, T* __restrict__ y,
-                 float* __restrict__ h_last, float* __restrict__ sumP, float* __restrict__ sumS,
+                 float* __restrict__ h_last, float* __restrict__ sumT, float* __restrict__ sumS,
                  const float* __restrict__ dt_bias, const SweepDims dm) {
   constexpr int G = N / NS;
   constexpr int kP = row_group<T, NS>();
@@ -444,13 +444,12 @@ __global__ void __launch_bounds__(64 * (N / NS))
   asm volatile("" ::"v"(pf_sink ^ pf_last));
 
   if (SUMMARY) {
-    if (sumP != nullptr && dvalid) {
-      const int64_t o = (((int64_t)chunk * dm.batch + b) * DI + d) * N + n0;
+    if (sumS != nullptr && dvalid) {
+      const int64_t row = ((int64_t)chunk * dm.batch + b) * DI + d;
+      // The chunk's decay products are exp2(Al2[n] * dsum); the carry forms them.
+      if (wv == 0) sumT[row] = dsum;
 #pragma unroll
-      for (int n = 0; n < NS; ++n) {
-        sumP[o + n] = hw_exp2(Al2[n] * dsum);
-        sumS[o + n] = h[n];
-      }
+      for (int n = 0; n < NS; ++n) sumS[row * N + n0 + n] = h[n];
     }
   } else if (h_last != nullptr && chunk == dm.n_chunks - 1 && dvalid) {
     float* hp = h_last + (b * DI + d) * N + n0;
@@ -474,16 +473,17 @@ hipError_t launch_scan_t(const ScanLaunch& p) {
   T* y = static_cast<T*>(p.y);
   hipError_t e;
   if (p.n_chunks > 1) {
-    float* sumP = p.workspace;
-    float* sumS = sumP + (p.n_chunks - 1) * states;
+    float* sumT = p.workspace;
+    float* sumS = sumT + scan_stepsum_floats(p.n_chunks, p.batch * p.d_inner);
     float* hent = sumS + (p.n_chunks - 1) * states;
     SweepDims ds = dm;
     ds.n_chunks_grid = (int32_t)(p.n_chunks - 1);
     ds.ckpt = nullptr;  // the summaries start from zero: only the main sweep writes checkpoints
     e = launch(k_scan_sweep<T, N, NS, true, MODE>, dim3((unsigned)(p.batch * (p.n_chunks - 1) * tiles)), dim3(64 * G), 0,
-               p.stream, x, dl, p.A, Bm, Cm, p.D, zz, (const float*)nullptr, y, p.h_last, sumP, sumS, p.dt_bias, ds);
+               p.stream, x, dl, p.A, Bm, Cm, p.D, zz, (const float*)nullptr, y, p.h_last, sumT, sumS, p.dt_bias, ds);
     if (e != hipSuccess) return e;
-    e = launch_chunk_carry(p.h0, sumP, sumS, hent, states, p.n_chunks, p.stream);
+    e = launch_chunk_carry(p.h0, p.A, (MODE & kLinearA) != 0, sumT, sumS, hent, p.batch * p.d_inner, N, p.d_inner,
+                           p.n_chunks, p.stream);
     if (e != hipSuccess) return e;
     dm.n_chunks_grid = (int32_t)p.n_chunks;
     dm.h_init_chunked = 1;

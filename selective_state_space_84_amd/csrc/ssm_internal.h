@@ -74,12 +74,15 @@ struct ConvLaunch {
   hipStream_t stream;
 };
 
-// Workspace layout used when n_chunks > 1, in floats, with S = batch*d_inner*d_state:
-//   [0, (n_chunks-1)*S)             chunk decay products  P[c][b][d][n]
-//   [(n_chunks-1)*S, 2(n_chunks-1)*S) chunk end states from zero  S[c][b][d][n]
-//   [2(n_chunks-1)*S, ...+n_chunks*S) chunk entry states  H[c][b][d][n]
-inline int64_t scan_workspace_floats(int64_t n_chunks, int64_t states) {
-  return n_chunks > 1 ? (3 * n_chunks - 2) * states : 0;
+// Workspace layout used when n_chunks > 1, in floats, with R = batch*d_inner
+// rows and S = R*d_state states (each section 256-byte aligned):
+//   [0, up((n_chunks-1)*R))      chunk step sums  T[c][b][d] (sum of the chunk's steps)
+//   next (n_chunks-1)*S           chunk end states from zero  S[c][b][d][n]
+//   next n_chunks*S               chunk entry states  H[c][b][d][n]
+// A chunk's decay products exp(A[d][n] * T[c][b][d]) are formed where they
+// are used, so one float per row replaces d_state of them.
+inline int64_t scan_stepsum_floats(int64_t n_chunks, int64_t rows) {
+  return n_chunks > 1 ? ((n_chunks - 1) * rows + 63) / 64 * 64 : 0;
 }
 
 // Gradient of the scan (one launch sequence).  io tensors (x, delta, z, dy,
@@ -133,12 +136,13 @@ BwdPlan bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner);
 // Sections of the backward workspace (floats, each 256-byte aligned), with
 // S = batch * d_inner * d_state states and c = n_chunks.  When the caller
 // passes the forward call's checkpoints (ckpt_given), the sections that only
-// serve to compute them (ckpt, fP, fS, fH) are left out.
+// serve to compute them (ckpt, fT, fS, fH) are left out.
 //   ckpt    [batch][ceil(seqlen/8)][d_state][d_inner]  states at block starts
 //   part_bc [tiles][batch][seqlen][2*d_state]          per-tile dB | dC sums
 //   part_a  [c][batch][d_inner][d_state]               per-(chunk, row) dA
 //   part_d, part_t [c][batch][d_inner]                 per-(chunk, row) dD, d_dt_bias
-//   when c > 1: forward chunk summaries fP, fS [c-1][S] and entry states fH
+//   when c > 1: forward chunk step sums fT [c-1][batch][d_inner], zero-start
+//   end states fS [c-1][S] and entry states fH
 //   [c][S]; adjoint chunk summaries lP, lS [c-1][S] and incoming adjoints
 //   lIn [c][S];
 //   when d_state > 16: part_el [3][batch][seqlen][d_inner], the state groups'
@@ -149,7 +153,7 @@ struct BwdWorkspace {
   float* part_a;
   float* part_d;
   float* part_t;
-  float* fP;
+  float* fT;
   float* fS;
   float* fH;
   float* lP;
@@ -185,8 +189,12 @@ hipError_t launch_ssd(const SsdLaunch& p);
 hipError_t launch_scan(const ScanLaunch& p);
 template <int MODE>
 hipError_t launch_scan_mode(const ScanLaunch& p);  // one translation unit per MODE
-hipError_t launch_chunk_carry(const float* h0, const float* sumP, const float* sumS, float* h_entry, int64_t states,
-                              int64_t n_chunks, hipStream_t stream);
+// Entry states of every chunk from the step sums T and zero-start end states
+// S of the chunks before it; A is read as the sweep reads it (structured when
+// linear_a).
+hipError_t launch_chunk_carry(const float* h0, const float* A, bool linear_a, const float* sumT, const float* sumS,
+                              float* h_entry, int64_t rows, int64_t d_state, int64_t d_inner, int64_t n_chunks,
+                              hipStream_t stream);
 hipError_t launch_state_fill(float* dst, const float* src, int64_t states, hipStream_t stream);
 hipError_t launch_update(const UpdateLaunch& p);
 hipError_t launch_conv1d(const ConvLaunch& p);

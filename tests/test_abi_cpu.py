@@ -86,7 +86,7 @@ def test_scan_argument_errors(lib):
     # A split sequence needs workspace of the queried size, 256-byte aligned.
     o = bd.ScanOpts(0, 0, 2, 0, 0, None)
     need = lib.ssm_scan_fwd_ex_workspace_size(2, 4, 8, 16, ctypes.byref(o))
-    assert need == (3 * 2 - 2) * 2 * 8 * 16 * 4
+    assert need == (64 + (2 * 2 - 1) * 2 * 8 * 16) * 4   # step sums (rounded to 64) + 3 state sets
     assert _scan(lib, opts=o) == bd.SSM_ERR_WORKSPACE
     assert _scan(lib, opts=o, ws=P0 + 20 * MB, ws_bytes=need - 4) == bd.SSM_ERR_WORKSPACE
     assert _scan(lib, opts=o, ws=P0 + 20 * MB + 16, ws_bytes=need) == bd.SSM_ERR_MISALIGNED
@@ -106,7 +106,7 @@ def test_noalloc_scan_checks_before_any_launch(lib):
     assert na(2, 4, 8, 16, 0, x=None) == bd.SSM_ERR_NULL_ARG
     assert na(2, 4, 8, 3, 0) == bd.SSM_ERR_UNSUPPORTED
     assert na(2, 4, 8, 16, 0, x=P0 + 1) == bd.SSM_ERR_MISALIGNED
-    # 16 chunks of 8 steps at 64 x 4096 x 16 states: 46 * 4M floats = 736 MiB of carries.
+    # 16 chunks of 8 steps at 64 x 4096 x 16 states: 31 sets of 4M states = 496 MiB of carries.
     assert na(64, 128, 4096, 16, 8) == bd.SSM_ERR_WORKSPACE
     assert na(64, 128, 4096, 16, 8, dtype=0) == bd.SSM_ERR_WORKSPACE
 
@@ -153,7 +153,9 @@ def test_launch_plan(lib, shape, expect_split, expect_chunks):
     assert g == expect_split
     assert nc == expect_chunks
     assert cl * nc >= shape[1] > cl * (nc - 1)
-    assert bd.scan_workspace_size(*shape) == (0 if nc == 1 else (3 * nc - 2) * shape[0] * shape[2] * shape[3] * 4)
+    rows = shape[0] * shape[2]
+    want = 0 if nc == 1 else (-(-(nc - 1) * rows // 64) * 64 + (2 * nc - 1) * rows * shape[3]) * 4
+    assert bd.scan_workspace_size(*shape) == want
 
 
 def test_plan_respects_overrides(lib):
@@ -226,10 +228,12 @@ def test_bwd_workspace_size(lib):
     cb = -(-nblk // min(-(-16384 // (b * tiles)), L // 64))
     nch = -(-nblk // cb)
     assert nch > 1
-    sums = 2 * up((nch - 1) * S) + up(nch * S)  # P, S, entry states: forward and adjoint sets alike
-    full = (up(b * nblk * N * d) + up(tiles * b * L * 2 * N) + up(nch * S) + 2 * up(nch * b * d) + 2 * sums) * 4
+    # Forward: step sums (one per row), end states, entry states; adjoint: P, S, incoming adjoints.
+    fsums = up((nch - 1) * b * d) + up((nch - 1) * S) + up(nch * S)
+    lsums = 2 * up((nch - 1) * S) + up(nch * S)
+    full = (up(b * nblk * N * d) + up(tiles * b * L * 2 * N) + up(nch * S) + 2 * up(nch * b * d) + fsums + lsums) * 4
     assert lib.ssm_scan_bwd_workspace_size(b, L, d, N) == full
-    assert lib.ssm_scan_bwd_workspace_size_ex(b, L, d, N, 1) == full - (up(b * nblk * N * d) + sums) * 4
+    assert lib.ssm_scan_bwd_workspace_size_ex(b, L, d, N, 1) == full - (up(b * nblk * N * d) + fsums) * 4
 
 
 def test_bwd_argument_errors(lib):

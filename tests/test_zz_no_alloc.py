@@ -76,22 +76,27 @@ def test_two_calls_in_a_row_second_smaller(lib):
 
 
 def test_plan_capped_to_the_scratch(lib):
-    """The Mamba-130M layer shape: its automatic plan (32 chunks) needs more
-    carries than the scratch holds, so the no-allocation call keeps 29 chunks
-    of 72 steps; it equals the workspace entry point run with that chunk
-    length, and the default 32-chunk plan within the bf16 gate."""
+    """The Mamba-130M layer's widths at 4096 steps (8 x 4096 x 1536 x 16): its
+    automatic plan (64 chunks of 64 steps) needs more carries than the
+    scratch holds, so the no-allocation call keeps 40 chunks of 104 steps
+    (41 would fit: 104-step chunks make 40); it equals the workspace entry
+    point run with that chunk length, and the default plan within the bf16
+    gate."""
     import torch
     from gpu_util import to_host_f64
-    cfg = inputs.MAMBA_130M
-    batch, L, d_inner, N = cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state
+    batch, L, d_inner, N = 8, 4096, 1536, 16
+    assert binding.scan_plan(batch, L, d_inner, N)[1:] == (64, 64)
     assert lib.ssm_scan_fwd_workspace_size(batch, L, d_inner, N) > lib.ssm_scan_fwd_noalloc_max_bytes()
+    o = binding.ScanOpts(0, 0, 104, 0, 0, None, None)
+    assert lib.ssm_scan_fwd_ex_workspace_size(batch, L, d_inner, N, ctypes.byref(o)) <= \
+        lib.ssm_scan_fwd_noalloc_max_bytes()
     print("case noalloc capped plan", flush=True)
     inp = inputs.make_scan_inputs(batch, L, d_inner, N, "bf16", 6102, params="random")
     d, y_na, h_na = _run_both(lib, inp, 1)
-    y72, h72 = _ex(lib, d, batch, L, d_inner, N, 1, 72)
+    y104, h104 = _ex(lib, d, batch, L, d_inner, N, 1, 104)
     y0, h0 = _ex(lib, d, batch, L, d_inner, N, 1, 0)
     torch.cuda.synchronize()
-    assert torch.equal(y_na, y72) and torch.equal(h_na, h72)
+    assert torch.equal(y_na, y104) and torch.equal(h_na, h104)
     assert floored_rel_err(to_host_f64(y_na), to_host_f64(y0)) <= 2e-2
     assert floored_rel_err(to_host_f64(h_na), to_host_f64(h0)) <= 2e-2
     # A few whole channels against the oracle.
