@@ -14,7 +14,9 @@
 //   H'  = exp(l_Q) H + B^T (w o X)            w_i = exp(l_Q - l_i) dt_i
 // Folding D_h into the diagonal of W gives the skip term for free.  The four
 // products run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation, and the
-// state stays in fp32 accumulators for the whole sequence.
+// state stays in fp32 accumulators for the whole sequence, kept scaled by a
+// power of two so that the decay exp(l_Q) is folded into w and exp(l) and
+// applied to the accumulators only when the scale is reset.
 //
 // Precision: x, B, C are bf16 inputs and enter the products exactly.  The
 // derived operands (W, the state fed to C H, and w o X) are sums of terms much
@@ -149,6 +151,8 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   __shared__ __align__(16) uint16_t sC[2][kQ * SC];
   __shared__ __align__(16) uint16_t sW[2][kQ * kSW];  // masked scores [k][i], hi and lo planes
   __shared__ __align__(16) float sv[2][4][kQ];         // l (log2 units), dt, w, exp(l); double-buffered
+  __shared__ float sfac[2];                            // per chunk: state rescale factor (negative: none)
+  __shared__ float slam;                               // log2 of the scale of the kept state, at the end
   __shared__ __align__(16) uint16_t sZY[kQ * kSZ];    // gate inputs in, outputs out, row-major
 
   const int tid = threadIdx.x;
@@ -263,6 +267,15 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   // Steps and decay sums of chunk cc (lane = step) into sv[cc & 1], by wave 3
   // (the one without a score tile), a chunk ahead of their use.  Steps past
   // the end count as dt = 0: decay 1, no input.
+  // The state is kept scaled, G = H 2^-lam with lam the log2 of the decay
+  // since the last rescale, so that a chunk adds to it without multiplying it
+  // by the chunk's decay first: G += B^T (w' o X) with w'_i = 2^(-lam - l_i)
+  // dt_i (lam before the chunk), and C H enters the outputs as
+  // 2^(l_k + lam) C G.  When the scale would pass 2^60 the chunk rescales G to
+  // H instead (factor 2^(lam + l_Q), passed on in sfac) and takes the unscaled
+  // weights 2^(l_Q - l_i) dt_i, so no weight and no kept state exceeds 2^60
+  // times its unscaled size.
+  float lam = 0.f;  // wave 3's running lam
   auto decay_sums = [&](int64_t cc) {
     const int ntc = (int)min((int64_t)kQ, L - cc * kQ);
     float d = 0.f;
@@ -272,13 +285,17 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     }
     const float l = scan32(d * Al2);
     const float lq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), kQ - 1));
+    const bool rescale = lam + lq < -60.f;
+    const float sigma = rescale ? lq : -lam;
     if (lane < kQ) {
       float* const sd = &sv[cc & 1][0][0];
       sd[lane] = l;
       sd[kQ + lane] = d;
-      sd[2 * kQ + lane] = hw_exp2(lq - l) * d;
-      sd[3 * kQ + lane] = hw_exp2(l);
+      sd[2 * kQ + lane] = hw_exp2(sigma - l) * d;
+      sd[3 * kQ + lane] = hw_exp2(l + lam);
     }
+    if (lane == 0) sfac[cc & 1] = rescale ? hw_exp2(lam + lq) : -1.f;
+    lam = rescale ? 0.f : lam + lq;
   };
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
@@ -312,7 +329,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     const float* const dv = lv + kQ;
     const float* const wv = lv + 2 * kQ;
     const float* const ev = lv + 3 * kQ;
-    const float decay = hw_exp2(lv[kQ - 1]);
+    const float fac = sfac[buf];
 
     // 2. Score tile (it, kt) = (0,0), (0,1), (1,1) for waves 0, 1, 2:
     //    S^T = B C^T over the permuted state order, masked into W.
@@ -393,7 +410,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
       *yz = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
     }
 
-    // 5. State: H = exp(l_Q) H + B^T (w o X).
+    // 5. State: G += B^T (w' o X), after the rescale when the chunk has one.
     u16x8 xwh, xwl;
     {
       const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wv[8 * q4]);
@@ -410,11 +427,15 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
       xwh = as_u16x8(vh);
       xwl = as_u16x8(vl);
     }
+    if (fac >= 0.f) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) accH[nt] *= fac;
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int n = 16 * nt + r16;
       const u16x8 bt = *reinterpret_cast<const u16x8*>(&sBt[(n >> 2) * GT + (n & 3) * kQ + 8 * q4]);
-      f32x4 acc = accH[nt] * decay;
+      f32x4 acc = accH[nt];
       acc = mma(bt, xwh, acc);
       acc = mma(bt, xwl, acc);
       accH[nt] = acc;
@@ -422,6 +443,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     if (w == 3 && c + 1 < nchunks) decay_sums(c + 1);
   }
 
+  if (w == 3 && lane == 0) slam = lam;
   // The last chunk's outputs (its first nt rows).
   __syncthreads();
   if (nchunks > 0) {
@@ -437,7 +459,7 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) hp[16 * nt + j] = accH[nt][j];
+      for (int j = 0; j < 4; ++j) hp[16 * nt + j] = accH[nt][j] * hw_exp2(slam);
   }
 }
 

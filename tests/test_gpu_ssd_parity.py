@@ -75,6 +75,19 @@ def test_ssd_long_sequence_state_carry(lib):
     _check(_gpu(inp), _ref(inp), "ssd L=4096")
 
 
+@pytest.mark.parametrize("d_state", [64, 128])
+def test_ssd_decay_extremes(lib, d_state):
+    """Heads whose decay over a 32-step chunk spans the kept state's scale
+    range: almost none (A = -0.005: the scale never resets over 4096 steps),
+    moderate (A = -1, -4: it resets every few dozen chunks) and total (A = -16
+    with steps of 0.9: a chunk decays by 2^-660, the state is reset to the new
+    chunk's inputs every chunk).  Against the oracle, with h0 != 0."""
+    inp = inputs.make_ssd_inputs(2, 4096, 4, 64, 1, d_state, 2500 + d_state, nonzero_h0=True)
+    inp["A"] = np.array([-0.005, -1.0, -4.0, -16.0], dtype=np.float32)
+    inp["dt"][:, :, 3] = inputs.f32_to_bf16_bits(np.full(inp["dt"].shape[:2], 0.9, dtype=np.float32))
+    _check(_gpu(inp), _ref(inp), "ssd decay extremes N=%d" % d_state)
+
+
 def test_ssd_split_resume(lib):
     """Scanning [0, s) then [s, L) from the handed-over state equals one scan."""
     import torch
