@@ -263,12 +263,13 @@ __global__ void __launch_bounds__(64 * (N / NS))
       if (!SUMMARY && own(i)) zn[i] = buf_ld<T>(rz, lo, so);
     }
   };
-  auto store_y = [&](int i, float v) {
-    // Narrowed in registers (RNE for bf16) and stored through the block's resource.
+  auto store_y = [&](uint32_t so, float v) {
+    // Narrowed in registers (RNE for bf16) and stored through the block's
+    // resource, row so bytes into the block.
     if constexpr (sizeof(T) == 2) {
-      buf_st(__builtin_bit_cast(uint16_t, (__bf16)v), block_rsrc(yb, blk_span), lo, (uint32_t)i * row_bytes);
+      buf_st(__builtin_bit_cast(uint16_t, (__bf16)v), block_rsrc(yb, blk_span), lo, so);
     } else {
-      buf_st(v, block_rsrc(yb, blk_span), lo, (uint32_t)i * row_bytes);
+      buf_st(v, block_rsrc(yb, blk_span), lo, so);
     }
   };
   fetch(0, std::integral_constant<bool, true>{});
@@ -304,21 +305,23 @@ __global__ void __launch_bounds__(64 * (N / NS))
       }
       ck += ck_step;
     }
-    T xr[kTB], dr[kTB], zr[kTB];
-#pragma unroll
-    for (int i = 0; i < kTB; ++i) {
-      xr[i] = xn[i];
-      dr[i] = dn[i];
-      zr[i] = zn[i];
-    }
+    // xn, dn, zn hold this block's rows; each is reloaded with the next
+    // block's row right after its last use here, in place.
     xb += blk_bytes;
     db += blk_bytes;
     zb += blk_bytes;
-    if (kFull) {
-      fetch(tb + kTB, std::integral_constant<bool, false>{});
-    } else if (tb + kTB < nsteps) {
-      fetch(tb + kTB, std::integral_constant<bool, true>{});
-    }
+    const bool more = kFull || tb + kTB < nsteps;
+    const __amdgpu_buffer_rsrc_t rxn = block_rsrc(xb, blk_span), rdn = block_rsrc(db, blk_span),
+                                 rzn = block_rsrc(zb, blk_span);
+    // The row stride re-read through an empty asm each block: the row
+    // offsets below are then formed where they are used (scalar multiplies)
+    // instead of being kept in registers across the loop.
+    uint32_t rbk = row_bytes;
+    asm volatile("" : "+s"(rbk));
+    auto next_so = [&](int i) {
+      const int ii = kFull ? i : min(tb + kTB + i, nsteps - 1) - (tb + kTB);
+      return (uint32_t)ii * rbk;
+    };
     pf_sink ^= pf_last;
     if (lane < 16) {
       const int tt = min(tb + kFar + (lane & 7), nsteps - 1);
@@ -328,8 +331,12 @@ __global__ void __launch_bounds__(64 * (N / NS))
 
     float part[kTB];
     auto step = [&](int i, const StateRow<T, NS>& bc, const StateRow<T, NS>& cc) {
-      const float xv = io_to_f32(xr[i]);
-      float dv = io_to_f32(dr[i]);
+      const float xv = io_to_f32(xn[i]);
+      float dv = io_to_f32(dn[i]);
+      if (more) {
+        xn[i] = buf_ld<T>(rxn, lo, next_so(i));
+        dn[i] = buf_ld<T>(rdn, lo, next_so(i));
+      }
       if (MODE & kSoftplusDelta) dv = softplus(dv, dtb);
       const float wx = dv * xv;
       float acc = Dv * xv;
@@ -405,12 +412,16 @@ __global__ void __launch_bounds__(64 * (N / NS))
         // of being sunk into per-step branches.
         if (has_z) {
 #pragma unroll
-          for (int i = 0; i < kTB; ++i) part[i] *= silu(io_to_f32(zr[i]));
+          for (int i = 0; i < kTB; ++i) part[i] *= silu(io_to_f32(zn[i]));
+        }
+        if (more) {
+#pragma unroll
+          for (int i = 0; i < kTB; ++i) zn[i] = buf_ld<T>(rzn, lo, next_so(i));
         }
         if (dvalid) {
 #pragma unroll
           for (int i = 0; i < kTB; ++i)
-            if (kFull || i < nt) store_y(i, part[i]);
+            if (kFull || i < nt) store_y((uint32_t)i * rbk, part[i]);
         }
       } else {
         float* mine = red + ((buf * G + wv) * kTB) * 64 + lane;
@@ -424,9 +435,14 @@ __global__ void __launch_bounds__(64 * (N / NS))
             float v = 0.f;
 #pragma unroll
             for (int j = 0; j < G; ++j) v += base[(j * kTB + i) * 64];
-            if (has_z) v *= silu(io_to_f32(zr[i]));
-            if (dvalid) store_y(i, v);
+            if (has_z) v *= silu(io_to_f32(zn[i]));
+            if (dvalid) store_y((uint32_t)i * row_bytes, v);
           }
+        }
+        if (more) {
+#pragma unroll
+          for (int i = 0; i < kTB; ++i)
+            if (own(i)) zn[i] = buf_ld<T>(rzn, lo, next_so(i));
         }
         buf ^= 1;
       }
