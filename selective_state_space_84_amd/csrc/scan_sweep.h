@@ -91,8 +91,6 @@ __device__ __forceinline__ void linear_decays(float y, float (&q)[NS]) {
 }
 
 constexpr int kTB = kTimeBlock;
-// Steps ahead of the current block whose B/C lines are warmed into L2.
-constexpr int kFar = 3 * kTB;
 
 // Steps per scalar-load group: keeps the two groups of B/C rows in flight
 // within ~32 SGPRs (bf16 rows are NS/2 dwords each for B and for C), which
@@ -274,11 +272,6 @@ __global__ void __launch_bounds__(64 * (N / NS))
   };
   fetch(0, std::integral_constant<bool, true>{});
 
-  // L2 warm-up: 16 lanes touch the B and C rows kFar steps ahead with vector
-  // loads (no scalar-counter wait); the value is folded into a sink so the
-  // loads are kept, and consumed a block later when they have long landed.
-  uint32_t pf_sink = 0, pf_last = 0;
-
   float dsum = 0.f;
   int buf = 0;
 
@@ -322,12 +315,6 @@ __global__ void __launch_bounds__(64 * (N / NS))
       const int ii = kFull ? i : min(tb + kTB + i, nsteps - 1) - (tb + kTB);
       return (uint32_t)ii * rbk;
     };
-    pf_sink ^= pf_last;
-    if (lane < 16) {
-      const int tt = min(tb + kFar + (lane & 7), nsteps - 1);
-      const T* src = ((lane & 8) && !SUMMARY) ? Cp + (int64_t)tt * N : Bp + (int64_t)tt * N;
-      pf_last = *reinterpret_cast<const uint32_t*>(src);
-    }
 
     float part[kTB];
     auto step = [&](int i, const StateRow<T, NS>& bc, const StateRow<T, NS>& cc) {
@@ -454,10 +441,9 @@ __global__ void __launch_bounds__(64 * (N / NS))
   for (; tb + 2 * kTB <= nsteps; tb += kTB) block(tb, std::true_type{});
   for (; tb < nsteps; tb += kTB) block(tb, std::false_type{});
 
-  // Let the last scalar and warm-up loads land before the wave ends.
+  // Let the last scalar loads land before the wave ends.
   bq[0].touch();
   if (!SUMMARY) cq[0].touch();
-  asm volatile("" ::"v"(pf_sink ^ pf_last));
 
   if (SUMMARY) {
     if (sumS != nullptr && dvalid) {
