@@ -364,40 +364,58 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     __syncthreads();  // W complete
     if (c + 1 < nchunks) fetch_xz(c + 1);
 
-    // 4. Y^T = X^T W^T + (H^T C^T) diag(exp(l)); gate; store.
-    u16x8 hhi[NK], hlo[NK];
+    // 4. Y^T = X^T W^T + (H^T C^T) diag(exp(l)); gate; store.  Software
+    //    pipelined over the 32-state slices: the C operands of slice kk + 1
+    //    are requested before slice kk's state is split into hi and lo and
+    //    multiplied, so the split's VALU work covers the LDS latency.
+    f32x4 accY[2], accO[2];
+    {
+      u16x8 wq[2][2];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      u32x4 vh, vl;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4& a = accH[2 * kk + (q >> 1)];
-        const uint2 sp = split2(a[2 * (q & 1)], a[2 * (q & 1) + 1]);
-        vh[q] = sp.x;
-        vl[q] = sp.y;
+      for (int kt = 0; kt < 2; ++kt) {
+        const int k = 16 * kt + r16;
+        wq[kt][0] = *reinterpret_cast<const u16x8*>(&sW[0][k * kSW + 8 * q4]);
+        wq[kt][1] = *reinterpret_cast<const u16x8*>(&sW[1][k * kSW + 8 * q4]);
       }
-      hhi[kk] = as_u16x8(vh);
-      hlo[kk] = as_u16x8(vl);
+      auto cfrag = [&](int kt, int kk) {
+        return *reinterpret_cast<const u16x8*>(&sC[buf][(16 * kt + r16) * SC + 32 * kk + 8 * q4]);
+      };
+      u16x8 cn[2] = {cfrag(0, 0), cfrag(1, 0)};
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        accY[kt] = mma(xt, wq[kt][0], f32x4{0.f, 0.f, 0.f, 0.f});
+        accY[kt] = mma(xt, wq[kt][1], accY[kt]);
+        accO[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const u16x8 cb0 = cn[0], cb1 = cn[1];
+        if (kk + 1 < NK) {
+          cn[0] = cfrag(0, kk + 1);
+          cn[1] = cfrag(1, kk + 1);
+        }
+        u32x4 vh, vl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4& a = accH[2 * kk + (q >> 1)];
+          const uint2 sp = split2(a[2 * (q & 1)], a[2 * (q & 1) + 1]);
+          vh[q] = sp.x;
+          vl[q] = sp.y;
+        }
+        const u16x8 hh = as_u16x8(vh), hl = as_u16x8(vl);
+        accO[0] = mma(hh, cb0, accO[0]);
+        accO[1] = mma(hh, cb1, accO[1]);
+        accO[0] = mma(hl, cb0, accO[0]);
+        accO[1] = mma(hl, cb1, accO[1]);
+      }
     }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int k = 16 * kt + r16;
-      const u16x8 whi = *reinterpret_cast<const u16x8*>(&sW[0][k * kSW + 8 * q4]);
-      const u16x8 wlo = *reinterpret_cast<const u16x8*>(&sW[1][k * kSW + 8 * q4]);
-      f32x4 accY = {0.f, 0.f, 0.f, 0.f};
-      accY = mma(xt, whi, accY);
-      accY = mma(xt, wlo, accY);
-      f32x4 accO = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        const u16x8 cb = *reinterpret_cast<const u16x8*>(&sC[buf][k * SC + 32 * kk + 8 * q4]);
-        accO = mma(hhi[kk], cb, accO);
-        accO = mma(hlo[kk], cb, accO);
-      }
       const float ek = ev[k];
       float v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = accY[j] + ek * accO[j];
+      for (int j = 0; j < 4; ++j) v[j] = accY[kt][j] + ek * accO[kt][j];
       // This lane's 8 bytes of the tile: its gate inputs, then its outputs.
       u32x2* const yz = reinterpret_cast<u32x2*>(&sZY[k * kSZ + 16 * w + 4 * q4]);
       if (kGate) {
@@ -431,14 +449,19 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) accH[nt] *= fac;
     }
+    {
+      auto bfrag = [&](int nt) {
+        const int n = 16 * nt + r16;
+        return *reinterpret_cast<const u16x8*>(&sBt[(n >> 2) * GT + (n & 3) * kQ + 8 * q4]);
+      };
+      u16x8 bn = bfrag(0);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = 16 * nt + r16;
-      const u16x8 bt = *reinterpret_cast<const u16x8*>(&sBt[(n >> 2) * GT + (n & 3) * kQ + 8 * q4]);
-      f32x4 acc = accH[nt];
-      acc = mma(bt, xwh, acc);
-      acc = mma(bt, xwl, acc);
-      accH[nt] = acc;
+      for (int nt = 0; nt < NT; ++nt) {
+        const u16x8 bt = bn;
+        if (nt + 1 < NT) bn = bfrag(nt + 1);
+        accH[nt] = mma(bt, xwh, accH[nt]);
+        accH[nt] = mma(bt, xwl, accH[nt]);
+      }
     }
     if (w == 3 && c + 1 < nchunks) decay_sums(c + 1);
   }
