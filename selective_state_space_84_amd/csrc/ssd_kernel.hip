@@ -206,14 +206,19 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     const int last = (int)min((int64_t)kQ, L - t0) - 1;
     const gchar* xb = uniform_ptr(x + ((b * L + t0) * dm.nheads + h) * kHP);
     rx = gldr<u16x8>(xb, __umul24((uint32_t)min(sx_t, last), rowb) + sx_c * 2);
-    const gchar* db = uniform_ptr(dt + (b * L + t0) * dm.nheads + h);
-    // The steps (lane = step), for wave 3, which turns them into decay sums.
-    if (w == 3) rdt = gldr<uint16_t>(db, __umul24((uint32_t)min(lane, last), (uint32_t)dm.nheads * 2));
     if (kGate) {
       // Gate inputs in whole rows, like x: they pass through LDS into the Y^T layout.
       const gchar* zb = uniform_ptr(z + ((b * L + t0) * dm.nheads + h) * kHP);
       rz = gldr<u16x8>(zb, __umul24((uint32_t)min(sx_t, last), rowb) + sx_c * 2);
     }
+  };
+  // The steps of chunk c (lane = step), for wave 3, which turns them into
+  // decay sums a chunk ahead of their use.
+  auto fetch_dt = [&](int64_t c) {
+    const int64_t t0 = c * kQ;
+    const int last = (int)min((int64_t)kQ, L - t0) - 1;
+    const gchar* db = uniform_ptr(dt + (b * L + t0) * dm.nheads + h);
+    rdt = gldr<uint16_t>(db, __umul24((uint32_t)min(lane, last), (uint32_t)dm.nheads * 2));
   };
   auto fetch = [&](int64_t c) {
     const int64_t t0 = c * kQ;
@@ -302,7 +307,11 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
   if (nchunks > 0) {
     fetch(0);
     fetch_xz(0);
-    if (w == 3) decay_sums(0);
+    if (w == 3) {
+      fetch_dt(0);
+      decay_sums(0);
+      if (nchunks > 1) fetch_dt(1);
+    }
   }
   for (int64_t c = 0; c < nchunks; ++c) {
     const int buf = (int)(c & 1);
@@ -323,6 +332,12 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
     }
     stage_bt();
     if (c + 1 < nchunks) fetch(c + 1);
+    // Wave 3 has no score tile: the next chunk's decay sums fill its wait for
+    // the second barrier (their steps were requested a chunk ago).
+    if (w == 3 && c + 1 < nchunks) {
+      decay_sums(c + 1);
+      if (c + 2 < nchunks) fetch_dt(c + 2);
+    }
 
     // 1. This chunk's decay sums (written by wave 3 before the barrier).
     const float* const lv = &sv[buf][0][0];
@@ -463,7 +478,6 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
         accH[nt] = mma(bt, xwl, accH[nt]);
       }
     }
-    if (w == 3 && c + 1 < nchunks) decay_sums(c + 1);
   }
 
   if (w == 3 && lane == 0) slam = lam;
