@@ -2,7 +2,7 @@
 carries in the library's per-device scratch) against ssm_scan_fwd_ex (the
 same scan with a caller workspace), through the C ABI: two calls in a row,
 the second smaller, then a shape whose automatic plan is capped to what the
-scratch holds."""
+scratch holds, then the entry point captured in a HIP graph and replayed."""
 import ctypes
 
 import numpy as np
@@ -106,3 +106,73 @@ def test_plan_capped_to_the_scratch(lib):
     ry, rh = oracle.scan_channels(inp, chans)
     assert floored_rel_err(to_host_f64(y_na[bi, :, di]), ry) <= 2e-2
     assert floored_rel_err(to_host_f64(h_na[bi, di]), rh) <= 2e-2
+
+
+def test_noalloc_scan_replays_from_a_graph(lib):
+    """ssm_scan_fwd_noalloc under HIP graph capture: the case it exists for.
+
+    A chunked plan (summary sweep, chunk carry, main sweep) is captured once into
+    a graph on torch's capture stream and replayed several times, with eager work
+    of the program's own and synchronizations between the replays; every replay
+    must give the eager call's result bit for bit, and the eager call must match
+    the oracle on sampled channels.  The inputs are rewritten in place between
+    replays (a graph replays on the same buffers) and the outputs are poisoned
+    first, so a replay that did not run, or ran on stale carries, is caught."""
+    import torch
+    from gpu_util import dev_inputs, to_host_f64
+    batch, L, d_inner, N = 2, 3000, 96, 16
+    g, cl, nc = binding.scan_plan(batch, L, d_inner, N)
+    assert nc > 1, "the case must split the sequence into chunks"
+    seeds = [6200, 6201, 6202]
+    sets = [inputs.make_scan_inputs(batch, L, d_inner, N, "bf16", s, nonzero_h0=True, params="random")
+            for s in seeds]
+    dev = [dev_inputs(s) for s in sets]
+    # Buffers the graph is captured on; each replay's inputs are copied into them.
+    d = {k: (v.clone() if v is not None else None) for k, v in dev[0].items()}
+    y = torch.empty_like(d["x"])
+    h = torch.empty((batch, d_inner, N), device="cuda:0")
+
+    def call():
+        binding.ssm_scan_fwd_noalloc(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], y=y,
+                                     h_last=h)
+
+    # Eager references (the first call also sets up the scratch's address).
+    refs = []
+    for dv in dev:
+        for k in d:
+            if d[k] is not None:
+                d[k].copy_(dv[k])
+        call()
+        torch.cuda.synchronize()
+        refs.append((y.clone(), h.clone()))
+    print("capturing", flush=True)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    other = torch.randn(1 << 20, device="cuda:0")
+    for rep in range(6):
+        i = rep % len(dev)
+        for k in d:
+            if d[k] is not None:
+                d[k].copy_(dev[i][k])
+        y.fill_(float("nan"))
+        h.fill_(float("nan"))
+        other.mul_(0.5).add_(1.0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print("replay", rep, "inputs", i, flush=True)
+        assert torch.equal(y, refs[i][0]) and torch.equal(h, refs[i][1]), (rep, i)
+    # The eager results themselves against the oracle, on sampled channels.
+    inp = sets[0]
+    chans = [(0, 0), (1, 95), (0, 47)]
+    ry, rh = oracle.scan_channels(inp, chans)
+    yr, hr = refs[0]
+    ys = np.stack([to_host_f64(yr[b, :, c]) for b, c in chans])
+    hs = np.stack([to_host_f64(hr[b, c]) for b, c in chans])
+    assert floored_rel_err(ys, ry) <= 2e-2 and floored_rel_err(hs, rh) <= 2e-2
