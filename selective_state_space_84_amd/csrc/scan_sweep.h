@@ -317,41 +317,38 @@ __global__ void __launch_bounds__(64 * (N / NS))
     };
 
     float part[kTB];
-    auto step = [&](int i, const StateRow<T, NS>& bc, const StateRow<T, NS>& cc) {
-      const float xv = io_to_f32(xn[i]);
-      float dv = io_to_f32(dn[i]);
-      if (more) {
-        xn[i] = buf_ld<T>(rxn, lo, next_so(i));
-        dn[i] = buf_ld<T>(rdn, lo, next_so(i));
-      }
+    // The step value and the decays of one step.  They depend on delta alone,
+    // so a group's are all formed before its state updates (see below).
+    auto decays = [&](int i, float& dv, float (&ab)[NS]) {
+      dv = io_to_f32(dn[i]);
+      if (more) dn[i] = buf_ld<T>(rdn, lo, next_so(i));
       if (MODE & kSoftplusDelta) dv = softplus(dv, dtb);
-      const float wx = dv * xv;
-      float acc = Dv * xv;
-      float lin[(MODE & kLinearA) ? NS : 1];
       if constexpr ((MODE & kLinearA) != 0) {
         const float y1 = dv * Al2_1;
-        linear_decays<NS>(y1, lin);
+        linear_decays<NS>(y1, ab);
         if constexpr (G > 1) {
           // Wave wv owns states n0 + 1 .. n0 + NS: scale r^(j+1) by r^n0.
           const float base = hw_exp2(y1 * (float)n0);
 #pragma unroll
-          for (int n = 0; n < NS; ++n) lin[n] *= base;
+          for (int n = 0; n < NS; ++n) ab[n] *= base;
         }
+      } else {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) ab[n] = hw_exp2(dv * Al2[n]);
       }
+    };
+    auto step = [&](int i, const StateRow<T, NS>& bc, const StateRow<T, NS>& cc, float dv, const float (&ab)[NS]) {
+      const float xv = io_to_f32(xn[i]);
+      if (more) xn[i] = buf_ld<T>(rxn, lo, next_so(i));
+      const float wx = dv * xv;
+      float acc = Dv * xv;
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
-        const float yv = dv * Al2[n];
-        float ab;
-        if constexpr ((MODE & kLinearA) != 0) {
-          ab = lin[n];
-        } else {
-          ab = hw_exp2(yv);
-        }
         if (MODE & kExactZoh) {
-          const float coef = zoh_coef(yv, ab, dv, ia[n]);
-          h[n] = __builtin_fmaf(coef, xv * bc.get(n), ab * h[n]);
+          const float coef = zoh_coef(dv * Al2[n], ab[n], dv, ia[n]);
+          h[n] = __builtin_fmaf(coef, xv * bc.get(n), ab[n] * h[n]);
         } else {
-          h[n] = __builtin_fmaf(ab, h[n], wx * bc.get(n));
+          h[n] = __builtin_fmaf(ab[n], h[n], wx * bc.get(n));
         }
         if (!SUMMARY) acc = __builtin_fmaf(cc.get(n), h[n], acc);
       }
@@ -387,9 +384,17 @@ __global__ void __launch_bounds__(64 * (N / NS))
       bnext += kP * N;
       cnext += kP * N;
       __builtin_amdgcn_sched_barrier(0);
+      // All the group's decays first, then its state updates: the
+      // exponentials of step j + 1 then issue ahead of step j's dependent
+      // multiply-adds instead of right before their own (Mamba-1.4B layer
+      // on MI355X: 1.76 -> 1.63 ms with general A).
+      float dvq[kP], abq[kP][NS];
+#pragma unroll
+      for (int j = 0; j < kP; ++j) decays(sb + j, dvq[j], abq[j]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < kP; ++j)
-        if (kFull || sb + j < nt) step(sb + j, bc[j], cc[j]);
+        if (kFull || sb + j < nt) step(sb + j, bc[j], cc[j], dvq[j], abq[j]);
     }
 
     if (!SUMMARY) {
