@@ -36,31 +36,43 @@ if REPO not in sys.path:
     sys.path.insert(0, REPO)
 
 HBM_PEAK_GBPS = 8000.0
-# VALU issue slots on MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one
-# full-rate fp32 lane-op per slot (packed fp32 is not used).
-VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
-# Minimum VALU slots per scan element on gfx950 for d_state = 16 (exp and rcp
-# are half rate: 2 slots).  Per state: mul (delta*A), exp (2), mul (delta*x*B),
-# FMA (state), FMA (readout) = 6.  Per element: widen x, widen delta,
-# delta*x, D*x, widen z, -z*log2e, exp (2), +1, rcp (2), z*r, y*silu, narrow y.
+# VALU lane-slots on MI355X: the published 157.3 TFLOP/s fp32 vector rate
+# counts an FMA as two flops, i.e. 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz =
+# 78.6 T full-rate fp32 lane-ops/s; a wave64 v_fmac_f32 occupies a SIMD for
+# two cycles (measured on the device: independent FMAs from two or more
+# waves per SIMD ran at 2.5-2.6 cycles each, clock and loop overhead
+# included; one wave alone issues one VALU instruction per ~4.7 cycles).
+# Transcendentals (exp, rcp) run at a quarter of that rate (measured 8.2
+# cycles per wave64 v_exp_f32 per SIMD) and count 4 slots.  Packed fp32 is
+# not used.
+VALU_PEAK_TSLOTS = 256 * 4 * 32 * 2.4e9 / 1e12
+TRANS_SLOTS = 4
+
+
+# Minimum VALU slots per scan element.  Per state: mul (delta*A), exp,
+# mul (delta*x*B), FMA (state), FMA (readout) = 4 + exp.  Per element: widen
+# x, delta and z, delta*x, D*x, -z*log2e, exp, +1, rcp, z*r, y*silu, narrow y
+# = 10 + 2 transcendentals.
 def scan_slots_per_element(d_state: int, linear_a: bool = False) -> int:
+    per_element = 10 + 2 * TRANS_SLOTS
     if not linear_a:
-        return 6 * d_state + 14
-    # Structured A (one wave per tile): exp2 at y, 2y, 4y, 8y, 16y (2 slots
-    # each) with their scalings, y = delta * A[d, 0] log2 e, the other decays
-    # as one product each; per state mul (delta*x*B), FMA (state), FMA (readout).
+        return (4 + TRANS_SLOTS) * d_state + per_element
+    # Structured A (one wave per tile): exp2 at y, 2y, 4y, 8y, 16y with their
+    # scalings, y = delta * A[d, 0] log2 e, the other decays as one product
+    # each; per state mul (delta*x*B), FMA (state), FMA (readout).
     n = min(d_state, 16)
     exps = 1 + (n > 1) + (n > 3) + (n > 7) + (n > 15)
-    return 2 * exps + (exps - 1) + 1 + (n - exps) + 3 * d_state + 14
+    return TRANS_SLOTS * exps + (exps - 1) + 1 + (n - exps) + 3 * d_state + per_element
 
 
 # Minimum VALU slots per element of the scan's backward pass with the decays
-# computed once: per state and step 7 for the forward recomputation (mul,
-# exp (2), mul, FMA, readout FMA, g*h row), 7 for the adjoint step (FMA, mul,
-# 3 FMA, dB row mul, lam*abar) and 2 for the channel sums of dB and dC; per
-# element ~30 (widening, two sigmoids, dz, dx, ddelta, narrowing).
+# computed once: per state and step 5 + exp for the forward recomputation
+# (mul, exp, mul, FMA, readout FMA, g*h row), 7 for the adjoint step (FMA,
+# mul, 3 FMA, dB row mul, lam*abar) and 2 for the channel sums of dB and dC;
+# per element 22 + 4 transcendentals (widening, two sigmoids, dz, dx, ddelta,
+# narrowing).
 def bwd_slots_per_element(d_state: int) -> int:
-    return 16 * d_state + 30
+    return (14 + TRANS_SLOTS) * d_state + 22 + 4 * TRANS_SLOTS
 
 
 # Sources each kernel family is built from; a traffic figure is reported only
@@ -671,8 +683,8 @@ def main():
         "roofline_alu": {"bound": "alu", "achieved": round(achieved_slots, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                          "unit": "Tslot/s", "frac": round(achieved_slots / VALU_PEAK_TSLOTS, 4),
                          "slots_per_element": slots,
-                         "note": "VALU issue slots of the sweep (exp and rcp 2 slots, non-packed fp32): the "
-                                 "bound this general-A scan actually meets; HBM is ~1/3 used"},
+                         "note": "VALU lane-slots of the sweep (exp and rcp 4 slots, non-packed fp32): the "
+                                 "bound of the general-A scan, whose slot roof lies at ~54% of the HBM roof"},
         "kernel_source_sha": sha,
         "input_gen_s": round(gen_s, 1),
     }

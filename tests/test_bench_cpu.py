@@ -43,8 +43,14 @@ def test_traffic_follows_the_kernel_sources():
 
 
 def test_valu_slot_model():
-    # General A: 6 slots per state (mul, exp = 2, mul, two FMAs) + 14 per element.
-    assert bench.scan_slots_per_element(16) == 110
-    # Structured A: exp2 at y, 2y, 4y, 8y, 16y (2 slots each), four scalings,
-    # y itself, 11 products, then 3 slots per state + 14 per element.
-    assert bench.scan_slots_per_element(16, linear_a=True) == 10 + 4 + 1 + 11 + 48 + 14 == 88
+    # The peak: 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz, half the 157.3 TFLOP/s
+    # fp32 vector rate (an FMA is two flops).
+    assert abs(bench.VALU_PEAK_TSLOTS - 157.3 / 2) < 0.1
+    # General A: 8 slots per state (mul, exp = 4, mul, two FMAs) + 18 per
+    # element (10 full-rate ops and the gate's exp and rcp).
+    assert bench.scan_slots_per_element(16) == 8 * 16 + 18 == 146
+    # Structured A: exp2 at y, 2y, 4y, 8y, 16y (4 slots each), four scalings,
+    # y itself, 11 products, then 3 slots per state + 18 per element.
+    assert bench.scan_slots_per_element(16, linear_a=True) == 20 + 4 + 1 + 11 + 48 + 18 == 102
+    # Backward: 18 per state and step + 38 per element.
+    assert bench.bwd_slots_per_element(16) == 18 * 16 + 38 == 326
