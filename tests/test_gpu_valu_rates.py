@@ -1,0 +1,70 @@
+"""The VALU issue rates behind bench.py's VALU-slot roof, measured on the device.
+
+bench.py prices the scan against 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz
+(half of MI355X's published 157.3 TFLOP/s fp32 vector rate: a wave64 fp32
+FMA occupies a SIMD for two cycles) with a transcendental at four slots.  This
+test times register-only streams (tests/valu_rate_probe.hip) and checks the
+two ratios that model rests on, which do not depend on the clock:
+- one wave alone issues a VALU instruction about every four cycles, so two
+  or more waves per SIMD complete FMAs about twice as fast;
+- v_exp_f32 runs at a quarter of the FMA rate.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def probe(tmp_path_factory):
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    so = str(tmp_path_factory.mktemp("valu") / "libvalu_rate_probe.so")
+    subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-shared", "-fPIC", "-Xclang",
+                    "-target-feature", "-Xclang", "-packed-fp32-ops", os.path.join(HERE, "valu_rate_probe.hip"),
+                    "-o", so], check=True, capture_output=True)
+    lib = ctypes.CDLL(so)
+    lib.valu_rate_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.valu_rate_probe.restype = ctypes.c_int
+    return lib
+
+
+def _ns_per_instruction(lib, kind, waves_per_simd, iters=2000):
+    """Kernel time per wave instruction per SIMD (64 instructions per iteration)."""
+    blocks = 1024 * waves_per_simd
+    out = torch.empty(blocks * 64, device="cuda")
+    assert out.numel() == blocks * 64
+    st = torch.cuda.current_stream().cuda_stream
+    best = None
+    for _ in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        assert lib.valu_rate_probe(kind, out.data_ptr(), blocks, iters, st) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    return best * 1e6 / (iters * 64 * waves_per_simd)
+
+
+def test_fma_and_exp_issue_rates(probe):
+    fma1 = _ns_per_instruction(probe, 0, 1)
+    fma4 = _ns_per_instruction(probe, 0, 4)
+    exp8 = _ns_per_instruction(probe, 1, 8)
+    fma8 = _ns_per_instruction(probe, 0, 8)
+    print("ns per wave64 instruction per SIMD: fma 1 wave %.3f, 4 waves %.3f, 8 waves %.3f; exp 8 waves %.3f "
+          "(x 2.4 GHz: %.2f, %.2f, %.2f, %.2f cycles)" % (fma1, fma4, fma8, exp8, fma1 * 2.4, fma4 * 2.4, fma8 * 2.4,
+                                                       exp8 * 2.4))
+    # Several waves per SIMD complete FMAs at least ~1.6x as fast as one wave.
+    assert fma4 < 0.65 * fma1
+    # At 2.4 GHz (the peak clock) a wave64 FMA from a full SIMD takes at most
+    # ~3 cycles: the SIMD is 32 lanes wide for fp32 FMA, not 16.
+    assert fma8 * 2.4 < 3.2
+    # Transcendentals: about four FMA times each.
+    assert 2.8 < exp8 / fma8 < 5.5
