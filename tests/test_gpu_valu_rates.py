@@ -7,7 +7,10 @@ test times register-only streams (tests/valu_rate_probe.hip) and checks the
 two ratios that model rests on, which do not depend on the clock:
 - one wave alone issues a VALU instruction about every four cycles, so two
   or more waves per SIMD complete FMAs about twice as fast;
-- v_exp_f32 runs at a quarter of the FMA rate.
+- v_exp_f32 runs at about a quarter of the FMA rate.
+It also times the scan's per-state mix (four full-rate operations and one
+exponential): at 2.4 GHz such a state costs 16 cycles of VALU time by the
+slot count, and the printed figure shows what a SIMD actually sustains.
 """
 import ctypes
 import os
@@ -35,8 +38,9 @@ def probe(tmp_path_factory):
     return lib
 
 
-def _ns_per_instruction(lib, kind, waves_per_simd, iters=2000):
-    """Kernel time per wave instruction per SIMD (64 instructions per iteration)."""
+def _ns_per_instruction(lib, kind, waves_per_simd, iters=2000, per_iter=64):
+    """Kernel time per wave instruction (or per unit: per_iter units per loop
+    iteration) per SIMD."""
     blocks = 1024 * waves_per_simd
     out = torch.empty(blocks * 64, device="cuda")
     assert out.numel() == blocks * 64
@@ -50,7 +54,7 @@ def _ns_per_instruction(lib, kind, waves_per_simd, iters=2000):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
         best = ms if best is None else min(best, ms)
-    return best * 1e6 / (iters * 64 * waves_per_simd)
+    return best * 1e6 / (iters * per_iter * waves_per_simd)
 
 
 def test_fma_and_exp_issue_rates(probe):
@@ -68,3 +72,9 @@ def test_fma_and_exp_issue_rates(probe):
     assert fma8 * 2.4 < 3.2
     # Transcendentals: about four FMA times each.
     assert 2.8 < exp8 / fma8 < 5.5
+    # The scan's state mix, per state update (16 per loop iteration).
+    st2 = _ns_per_instruction(probe, 2, 2, per_iter=16)
+    st8 = _ns_per_instruction(probe, 2, 8, per_iter=16)
+    print("scan state mix, ns per state per SIMD: 2 waves %.3f, 8 waves %.3f (x 2.4 GHz: %.1f, %.1f cycles; "
+          "slot count 4 x fma + 1 exp)" % (st2, st8, st2 * 2.4, st8 * 2.4))
+    assert 4 * fma8 + exp8 * 0.9 < st8 < 4 * (4 * fma8 + exp8)
