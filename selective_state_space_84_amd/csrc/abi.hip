@@ -16,11 +16,12 @@ int64_t update_grid_blocks(int64_t batch, int64_t d_inner, int32_t d_state);
 
 namespace {
 
-// Below this many waves an MI355X is underfilled (256 CUs x 4 SIMDs, two waves
-// per SIMD keep the VALU busy while one waits).  At or above it, cutting the
-// sequence into chunks costs more (the summary pass) than it gains (measured
-// on the Mamba-1.4B layer: 2048 waves unchunked 1.99 ms, 2 chunks 2.34 ms,
-// 4 chunks 2.41 ms; 2 waves per tile 2.04 ms).
+// Below this many waves an MI355X is underfilled (256 CUs x 4 SIMDs; one wave
+// issues a VALU instruction only every ~4 cycles, so a SIMD needs two to fill
+// its 2-cycle VALU).  At or above it, cutting the sequence into chunks costs
+// more (the summary pass) than it gains (measured on the Mamba-1.4B layer:
+// 2048 waves unchunked 1.64 ms, 2 chunks 2.11 ms, 4 chunks 2.22 ms; 2 waves
+// per tile 1.85 ms).
 constexpr int64_t kTargetWaves = 2048;
 // Once a sequence is cut, aim for this many waves: measured on MI355X, more
 // resident waves pay for the summary pass on the chunks (Mamba-2.8B long
