@@ -341,6 +341,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
   const float Dv = D != nullptr ? D[dc] : 0.f;
   const float dtb = (MODE & 1) ? dt_bias[dc] : 0.f;
   float accD = 0.f, accT = 0.f;
+  const int wslot = wave_slot_parity();  // for take_turn (ssm_device.h)
 
   // Addressing (as in the forward sweep): the io tensors share one layout,
   // so a block of kBB rows is one buffer resource per tensor (SGPRs), the
@@ -459,6 +460,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
   };
 
   auto block = [&](int k) {
+    take_turn(k, wslot);
     const int64_t t0 = (int64_t)k * kBB;
     const int nt = steps_of(k);
     const int nsub = (nt + SUB - 1) / SUB;  // sub-blocks holding steps

@@ -274,6 +274,7 @@ __global__ void __launch_bounds__(64 * (N / NS))
 
   float dsum = 0.f;
   int buf = 0;
+  const int wslot = wave_slot_parity();  // for take_turn (ssm_device.h)
 
   // One block of kTB steps starting at tb.  FULL: no clamping anywhere
   // (callers guarantee tb + 2 * kTB <= nsteps).
@@ -289,6 +290,7 @@ __global__ void __launch_bounds__(64 * (N / NS))
   auto block = [&](int tb, auto full_t) {
     constexpr bool kFull = decltype(full_t)::value;
     const int nt = kFull ? kTB : min(kTB, nsteps - tb);
+    take_turn(tb / kTB, wslot);
     if (ck != nullptr) {
       if (dvalid) {
         // The last state row starts below 2^32 - 2^28; no bound is needed.

@@ -313,7 +313,12 @@ k_ssd_fwd(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const
       if (nchunks > 1) fetch_dt(1);
     }
   }
+  // Up to three workgroups share a CU: their waves take turns at the higher
+  // priority, one chunk each (take_turn, ssm_device.h), so that no workgroup
+  // runs its last chunks alone (0.402 -> 0.388 ms on the Mamba-2 2.7B layer).
+  const int wslot = wave_slot_parity();
   for (int64_t c = 0; c < nchunks; ++c) {
+    take_turn((int)c, wslot);
     const int buf = (int)(c & 1);
     const int64_t t0 = c * kQ;
     stage(buf);

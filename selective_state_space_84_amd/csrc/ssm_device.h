@@ -21,6 +21,23 @@ __device__ __forceinline__ void io_store(float* p, float v) { *p = v; }
 // 2^v on the hardware transcendental unit (no range reduction or denormal
 // fix-up; results below the normal range flush towards zero).
 __device__ __forceinline__ float hw_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// Turn-taking between the waves that share a SIMD.  The issue arbiter favours
+// the older of two waves; with equal work per wave (the Mamba-1.4B layer's
+// scan and backward launch exactly two per SIMD) the older wave of the scan
+// finished in ~1370 us and the younger in ~1625 us, which then ran alone for
+// the last 15%.  Waves of odd and even slots (HW_ID bits 3:0, read through
+// hwreg(HW_REG_HW_ID, 0, 32)) instead take the higher priority in turns, one
+// block each: both then finish within ~5% of each other (scan 1.64 -> 1.56
+// ms, backward from checkpoints 7.30 -> 6.91 ms; results unchanged).
+__device__ __forceinline__ int wave_slot_parity() { return (int)(__builtin_amdgcn_s_getreg(4 | (31 << 11)) & 1u); }
+__device__ __forceinline__ void take_turn(int block, int parity) {
+  if ((block + parity) & 1) {
+    __builtin_amdgcn_s_setprio(1);
+  } else {
+    __builtin_amdgcn_s_setprio(0);
+  }
+}
 __device__ __forceinline__ float hw_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
 __device__ __forceinline__ float hw_log2(float v) { return __builtin_amdgcn_logf(v); }
 
