@@ -53,15 +53,16 @@ TRANS_SLOTS = 4
 # mul (delta*x*B), FMA (state), FMA (readout) = 4 + exp.  Per element: widen
 # x, delta and z, delta*x, D*x, -z*log2e, exp, +1, rcp, z*r, y*silu, narrow y
 # = 10 + 2 transcendentals.
-def scan_slots_per_element(d_state: int, linear_a: bool = False) -> int:
+def scan_slots_per_element(d_state: int, linear_a: bool = False, io_bf16: bool = False) -> int:
     per_element = 10 + 2 * TRANS_SLOTS
     if not linear_a:
         return (4 + TRANS_SLOTS) * d_state + per_element
-    # Structured A (one wave per tile): exp2 at y, 2y, 4y, 8y, 16y with their
-    # scalings, y = delta * A[d, 0] log2 e, the other decays as one product
-    # each; per state mul (delta*x*B), FMA (state), FMA (readout).
+    # Structured A (one wave per tile), y = delta * A[d, 0] log2 e: with fp32
+    # io exp2 at y, 2y, 4y, 8y, 16y with their scalings, the other decays as
+    # one product each; with bf16 io exp2 at y only and every other decay as
+    # one product.  Per state mul (delta*x*B), FMA (state), FMA (readout).
     n = min(d_state, 16)
-    exps = 1 + (n > 1) + (n > 3) + (n > 7) + (n > 15)
+    exps = 1 if io_bf16 else 1 + (n > 1) + (n > 3) + (n > 7) + (n > 15)
     return TRANS_SLOTS * exps + (exps - 1) + 1 + (n - exps) + 3 * d_state + per_element
 
 
@@ -230,7 +231,7 @@ def scan_record(cfg, ms, spread, plan, flags, h0, plan_is_default=True):
     io_bytes = 2 if cfg.dtype == "bf16" else 4
     alg = algorithmic_scan_bytes(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, io_bytes, h0, True)
     linear = bool(flags & binding.SSM_FLAG_A_LINEAR_N)
-    slots = scan_slots_per_element(cfg.d_state, linear)
+    slots = scan_slots_per_element(cfg.d_state, linear, cfg.dtype == "bf16")
     el_s = el / (ms * 1e-3)
     gbps = alg / (ms * 1e-3) / 1e9
     g, chunk_len, n_chunks = plan

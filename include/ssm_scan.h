@@ -98,9 +98,12 @@ enum {
                                         from principle to code" section 6.2).  The forward
                                         scan then reads only A[d][0] and evaluates the N
                                         decays exp(delta (n+1) A[d][0]) of an element from
-                                        five exponentials and products (about 1.25x fewer
-                                        vector instructions at d_state 16); results are
-                                        those of that A, to the same accuracy.  Never
+                                        products of five exponentials with fp32 io (the
+                                        general path's accuracy) or of one exponential with
+                                        bf16 io (the powers then carry up to ~20 ulp, far
+                                        below the rounding of bf16 outputs): about 1.4x
+                                        (fp32) or 1.7x (bf16) fewer vector instruction
+                                        slots at d_state 16.  Never
                                         inferred from A: only this flag selects it.  The
                                         decode update and the backward pass accept the flag
                                         and compute from the whole A. */

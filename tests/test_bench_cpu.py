@@ -52,5 +52,7 @@ def test_valu_slot_model():
     # Structured A: exp2 at y, 2y, 4y, 8y, 16y (4 slots each), four scalings,
     # y itself, 11 products, then 3 slots per state + 18 per element.
     assert bench.scan_slots_per_element(16, linear_a=True) == 20 + 4 + 1 + 11 + 48 + 18 == 102
+    # With bf16 io: exp2 at y only, y itself and 15 products.
+    assert bench.scan_slots_per_element(16, linear_a=True, io_bf16=True) == 4 + 1 + 15 + 48 + 18 == 86
     # Backward: 18 per state and step + 38 per element.
     assert bench.bwd_slots_per_element(16) == 18 * 16 + 38 == 326
