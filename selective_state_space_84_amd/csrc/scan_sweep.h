@@ -1,5 +1,5 @@
 // Selective-scan sweep kernel for gfx950 (MI355X), shared by the per-mode
-// translation units scan_mode{0..7}.hip.
+// translation units scan_mode{0,1,2,3}.hip.
 //
 // What is computed (per batch row b, channel d, state n; A diagonal):
 //   abar = exp(delta[b,t,d] * A[d,n])                     -- decay
