@@ -395,3 +395,65 @@ def make_conv_inputs(batch: int, seqlen: int, d_inner: int, d_conv: int, dtype: 
     out["state"] = (round_to_f32(np.random.default_rng(ks).standard_normal((batch, d_inner, d_conv - 1)))
                     if with_state else None)
     return out
+
+
+def _io_values(a: np.ndarray) -> np.ndarray:
+    """float32 values of an io tensor (bf16 bit patterns or float32)."""
+    return bf16_bits_to_f32(a) if a.dtype == np.uint16 else a.astype(np.float32)
+
+
+def _like_io(v: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    return f32_to_bf16_bits(v) if ref.dtype == np.uint16 else v
+
+
+def make_degenerate(inp: Dict[str, np.ndarray], seed: int, raw_delta: bool = False,
+                    keep_linear_a: bool = False) -> Dict[str, np.ndarray]:
+    """A copy of scan or decode inputs with the method's degenerate values
+    planted at seeded positions (every value below is exact in bf16):
+
+      * steps that stop time: delta = 0 on 5% of elements (with ``raw_delta``
+        the raw input -100, whose softplus lies below fp32's normal range);
+      * steps long enough that most decays underflow to zero: delta = 30 (raw
+        40) on 3% of elements, with x = 1/32 there so that delta * x stays of
+        order one;
+      * x = 0 on 3% of the other elements;
+      * gate inputs far into both tails: z = 60, -60 and -200 (e^200
+        overflows fp32) on 3% of elements each;
+      * whole rows of B, and of C, set to zero on 6% of (row, step) pairs;
+      * A = 0 (no decay) on every 19th channel and, unless ``keep_linear_a``
+        (inputs of the structured path, which must keep A[d, n] = (n + 1)
+        A[d, 0]), on every 7th channel's third state;
+      * D = 0 on every 5th channel and D negated on the channel after it.
+
+    Works on (batch, seqlen, .) scan tensors and on (steps, batch, .) decode
+    tensors alike: the positions are drawn per element of x and per row of B
+    and C from ``SeedSequence([seed, 0xDE6]).spawn(4)`` = [step, x, z, rows]."""
+    ks, kx, kz, kr = np.random.SeedSequence([seed, 0xDE6]).spawn(4)
+    out = dict(inp)
+    x, dl, z = (_io_values(inp[k]) for k in ("x", "delta", "z"))
+    B, C = _io_values(inp["B"]), _io_values(inp["C"])
+    u = np.random.default_rng(ks).random(x.shape)
+    dl[u < 0.05] = -100.0 if raw_delta else 0.0
+    big = (u >= 0.05) & (u < 0.08)
+    dl[big] = 40.0 if raw_delta else 30.0
+    x[big] = 1.0 / 32.0
+    x[(np.random.default_rng(kx).random(x.shape) < 0.03) & ~big] = 0.0
+    v = np.random.default_rng(kz).random(z.shape)
+    z[v < 0.03] = 60.0
+    z[(v >= 0.03) & (v < 0.06)] = -60.0
+    z[(v >= 0.06) & (v < 0.09)] = -200.0
+    rows = np.random.default_rng(kr).random((2,) + B.shape[:2])
+    B[rows[0] < 0.06] = 0.0
+    C[rows[1] < 0.06] = 0.0
+    for k, val in (("x", x), ("delta", dl), ("z", z), ("B", B), ("C", C)):
+        out[k] = _like_io(val, inp[k])
+    A = inp["A"].copy()
+    A[3::19, :] = 0.0
+    if not keep_linear_a and A.shape[1] > 2:
+        A[::7, 2] = 0.0
+    D = inp["D"].copy()
+    D[::5] = 0.0
+    D[1::5] = -D[1::5]
+    out["A"], out["D"] = A, D
+    return out

@@ -53,3 +53,35 @@ def test_ssd_random_skip_varies_per_head():
     D0 = np.full_like(inp["D"], inp["D"][0])
     my, _ = oracle.ssd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D0, inp["z"])
     assert floored_rel_err(my, ry) > 5 * 2e-2
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("raw_delta", [False, True])
+def test_degenerate_values_are_planted(dtype, raw_delta):
+    """inputs.make_degenerate puts each degenerate value where it says, keeps
+    the structured-A form when asked, and leaves the source inputs alone."""
+    inp = inputs.make_scan_inputs(2, 100, 130, 16, dtype, 9, nonzero_h0=True, raw_delta=raw_delta,
+                                  params="linear")
+    keep = {k: v.copy() for k, v in inp.items() if v is not None}
+    deg = inputs.make_degenerate(inp, 9, raw_delta=raw_delta, keep_linear_a=True)
+    for k, v in keep.items():
+        assert np.array_equal(inp[k], v), k
+    step = inputs._io_values(deg["delta"])
+    x, z = inputs._io_values(deg["x"]), inputs._io_values(deg["z"])
+    stop, big = (-100.0, 40.0) if raw_delta else (0.0, 30.0)
+    assert 0.03 < np.mean(step == stop) < 0.07 and 0.015 < np.mean(step == big) < 0.045
+    assert np.all(x[step == big] == 1.0 / 32.0) and np.mean(x == 0.0) > 0.02
+    for v in (60.0, -60.0, -200.0):
+        assert 0.015 < np.mean(z == v) < 0.045, v
+    for k in ("B", "C"):
+        rows = np.all(inputs._io_values(deg[k]) == 0.0, axis=-1)
+        assert 0.01 < rows.mean() < 0.15, k
+    A = deg["A"]
+    assert np.all(A[3::19] == 0.0)
+    n = np.arange(1, 17, dtype=np.float32)
+    assert np.array_equal(A, (n[None, :] * A[:, :1]).astype(np.float32))
+    D = deg["D"]
+    assert np.all(D[::5] == 0.0) and np.array_equal(D[1::5], -inp["D"][1::5])
+    # general inputs also get single zero states
+    gen = inputs.make_degenerate(inputs.make_scan_inputs(1, 10, 30, 16, dtype, 3), 3)
+    assert np.all(gen["A"][::7, 2] == 0.0)

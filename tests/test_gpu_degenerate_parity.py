@@ -1,0 +1,169 @@
+"""GPU parity on the method's degenerate values, against the fp64 oracle.
+
+The inputs are the usual seeded ones with degenerate values planted
+(inputs.make_degenerate): steps of zero length (the state is carried over
+unchanged, derivation page "Deriving and implementing Mamba from scratch"
+section 4.2: a small step keeps the state, a large one resets it to the
+current input), steps so long that the decays underflow to zero, channels
+with A = 0 (no decay: an undamped running sum), x = 0, whole B or C rows of
+zeros, D = 0 or negative, and gate inputs far into both tails of SiLU (z =
+-200 makes e^-z overflow fp32; the gate is then -0).  Every entry point of
+the recurrence meets them: the scan in every launch plan (unsplit, state
+split over lanes, sequence chunks), the structured-A path, the softplus and
+exact-ZOH step modes, the decode update and the backward pass.  Gates as
+elsewhere: fp32 io 1e-5 or the case's emulated fp32 floor
+(test_tolerance_floor.f32_gate), bf16 io 2e-2; the backward's gates from
+test_tolerance_bwd.  The planted values widen the outputs' range (a gate
+input of 60 scales an output 60-fold, an undamped channel's state keeps
+growing), so the floored error is taken per class, each with its own rms
+floor: outputs whose gate input lies in a tail (|z| >= 50) apart from the
+others, and states of channels with a zero entry of A apart from the others.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from conftest import floored_rel_err
+from selective_state_space_84_amd import binding, inputs
+from test_tolerance_bwd import BWD_F32_GATE
+from test_tolerance_floor import decode_f32_gate, f32_gate
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+SP = binding.SSM_FLAG_DELTA_SOFTPLUS
+ZOH = binding.SSM_FLAG_EXACT_ZOH
+LIN = binding.SSM_FLAG_A_LINEAR_N
+
+
+def _scan_case(dtype, seed, flags=0, params="random", L=100, d=200, N=16):
+    inp = inputs.make_scan_inputs(3, L, d, N, dtype, seed, nonzero_h0=True, raw_delta=bool(flags & SP),
+                                  params=params)
+    return inputs.make_degenerate(inp, seed, raw_delta=bool(flags & SP), keep_linear_a=bool(flags & LIN))
+
+
+def _class_err(got, ref, masks):
+    """Largest floored relative error over the classes (boolean masks)."""
+    return max(floored_rel_err(got[m], ref[m]) for m in masks if m.any())
+
+
+def _y_classes(inp, shape):
+    tail = np.abs(inputs._io_values(inp["z"])) >= 50.0
+    return [tail.reshape(shape), ~tail.reshape(shape)]
+
+
+def _h_classes(inp, shape):
+    undamped = np.broadcast_to((inp["A"] == 0.0).any(axis=1)[None, :, None], shape)
+    return [undamped, ~undamped]
+
+
+def _err_y(got, ref, case):
+    return _class_err(got, ref, _y_classes(case, ref.shape))
+
+
+def _err_h(got, ref, case):
+    return _class_err(got, ref, _h_classes(case, ref.shape))
+
+
+def _check_scan(inp, dtype, flags, **opts):
+    import torch
+    from gpu_util import dev_inputs, to_dev, to_host_f64
+    print("case degenerate scan", inp["x"].shape, dtype, flags, opts, flush=True)
+    d = dev_inputs(inp)
+    dtb = to_dev(inp["dt_bias"]) if flags & SP else None
+    y, hl = binding.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], flags=flags,
+                                 dt_bias=dtb, **opts)
+    torch.cuda.synchronize()
+    ry, rh = oracle.scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
+                         inp["dt_bias"] if flags & SP else None, exact_zoh=bool(flags & ZOH),
+                         delta_softplus=bool(flags & SP))
+    gy, gh = to_host_f64(y), to_host_f64(hl)
+    assert np.isfinite(gy).all() and np.isfinite(gh).all()
+    tol = f32_gate(inp, flags & (SP | ZOH), err_y=_err_y, err_h=_err_h) if dtype == "f32" else 2e-2
+    ey, eh = _err_y(gy, ry, inp), _err_h(gh, rh, inp)
+    print("  errors y %.2e h %.2e gate %.1e" % (ey, eh, tol), flush=True)
+    assert ey <= tol and eh <= tol, (ey, eh, tol)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_split,chunk_len", [(1, 0), (4, 0), (1, 24), (2, 13)])
+def test_scan_degenerate_values(lib, dtype, n_split, chunk_len):
+    inp = _scan_case(dtype, 8100 + 10 * n_split + chunk_len)
+    _check_scan(inp, dtype, 0, n_split=n_split, chunk_len=chunk_len)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_split,chunk_len", [(1, 0), (2, 0), (1, 24)])
+def test_scan_degenerate_values_structured_a(lib, dtype, n_split, chunk_len):
+    """A[d, 0] = 0 on whole channels keeps the S4D-real structure (all decays 1)."""
+    inp = _scan_case(dtype, 8200 + 10 * n_split + chunk_len, flags=LIN, params="linear")
+    _check_scan(inp, dtype, LIN, n_split=n_split, chunk_len=chunk_len)
+
+
+@pytest.mark.parametrize("flags", [SP, ZOH, SP | ZOH])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_degenerate_values_step_modes(lib, flags, dtype):
+    inp = _scan_case(dtype, 8300 + flags, flags=flags)
+    _check_scan(inp, dtype, flags)
+
+
+def test_scan_degenerate_values_large_d_state(lib):
+    inp = _scan_case("f32", 8400, L=40, d=70, N=64)
+    _check_scan(inp, "f32", 0)
+
+
+@pytest.mark.parametrize("flags", [0, SP, ZOH])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_degenerate_values(lib, flags, dtype):
+    import torch
+    from gpu_util import to_dev, to_host_f64
+    steps, batch, d, N = 8, 4, 300, 16
+    inp = inputs.make_decode_inputs(batch, d, N, dtype, steps, 8500 + flags, raw_delta=bool(flags & SP),
+                                    params="random")
+    inp = inputs.make_degenerate(inp, 8500 + flags, raw_delta=bool(flags & SP))
+    print("case degenerate decode", dtype, flags, flush=True)
+    A, D = to_dev(inp["A"]), to_dev(inp["D"])
+    dtb = to_dev(inp["dt_bias"]) if flags & SP else None
+    h = torch.zeros((batch, d, N), dtype=torch.float32, device="cuda:0")
+    hr = np.zeros((batch, d, N))
+    tol = decode_f32_gate(inp, steps, flags, err_y=_err_y, err_h=_err_h) if dtype == "f32" else 2e-2
+    for s in range(steps):
+        xs = {k: to_dev(np.ascontiguousarray(inp[k][s])) for k in ("x", "delta", "z", "B", "C")}
+        yt = binding.ssm_state_update(h, xs["x"], xs["delta"], A, xs["B"], xs["C"], D, xs["z"], flags=flags,
+                                      dt_bias=dtb)
+        torch.cuda.synchronize()
+        yr, hr = oracle.update(hr, inp["x"][s], inp["delta"][s], inp["A"], inp["B"][s], inp["C"][s], inp["D"],
+                               inp["z"][s], inp["dt_bias"] if flags & SP else None, exact_zoh=bool(flags & ZOH),
+                               delta_softplus=bool(flags & SP))
+        ey = _err_y(to_host_f64(yt), yr, {"z": inp["z"][s]})
+        assert ey <= tol, (s, ey, tol)
+    eh = _err_h(to_host_f64(h), hr, inp)
+    print("  state error %.2e gate %.1e" % (eh, tol), flush=True)
+    assert eh <= tol
+
+
+@pytest.mark.parametrize("flags", [0, SP, ZOH])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_degenerate_values(lib, flags, dtype):
+    import torch
+    from gpu_util import to_dev, to_host_f64
+    seed = 8600 + flags
+    inp = inputs.make_scan_inputs(2, 45, 130, 16, dtype, seed, nonzero_h0=True, raw_delta=bool(flags & SP),
+                                  params="random")
+    inp = inputs.make_degenerate(inp, seed, raw_delta=bool(flags & SP))
+    gr = inputs.make_scan_grads(2, 45, 130, 16, dtype, seed)
+    print("case degenerate bwd", dtype, flags, flush=True)
+    d = {k: to_dev(inp.get(k)) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "dt_bias")}
+    g = binding.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
+                             dy=to_dev(gr["dy"]), dh_last=to_dev(gr["dh_last"]), flags=flags,
+                             dt_bias=d["dt_bias"] if flags & SP else None, want_dh0=True)
+    torch.cuda.synchronize()
+    g = {k: to_host_f64(v) for k, v in g.items()}
+    r = oracle.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
+                        inp["dt_bias"] if flags & SP else None, dy=gr["dy"], dh_last=gr["dh_last"],
+                        delta_softplus=bool(flags & SP), exact_zoh=bool(flags & ZOH))
+    gate = BWD_F32_GATE if dtype == "f32" else 2e-2
+    errs = {k: floored_rel_err(g[k], r[k]) for k in r if k in g and r[k].size}
+    print("  " + " ".join("%s %.2e" % kv for kv in errs.items()), flush=True)
+    for k, e in errs.items():
+        assert np.isfinite(g[k]).all(), k
+        assert e <= gate, (k, e, gate)

@@ -161,29 +161,33 @@ def _emulate_steps(inp, softplus, zoh, ideal_softplus):
     return y, h
 
 
-def emulated_floor(inp, flags=0, ideal_softplus=False):
+def emulated_floor(inp, flags=0, ideal_softplus=False, err_y=None, err_h=None):
     """Floored error of the fp32 emulation of this case against the oracle
-    (max over y and h_last); bit 0 of flags: softplus step, bit 1: exact ZOH."""
+    (max over y and h_last); bit 0 of flags: softplus step, bit 1: exact ZOH.
+    err_y / err_h (got, ref, case) replace the error measure of y / h_last,
+    so that a test gating on another measure sizes its floor with that one."""
     softplus, zoh = bool(flags & 1), bool(flags & 2)
     y, h = _emulate(inp, softplus, zoh, ideal_softplus)
     ry, rh = oracle.scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
                          inp["dt_bias"] if softplus else None, delta_softplus=softplus, exact_zoh=zoh)
-    return max(floored_rel_err(y, ry), floored_rel_err(h, rh))
+    ey = err_y(y, ry, inp) if err_y is not None else floored_rel_err(y, ry)
+    eh = err_h(h, rh, inp) if err_h is not None else floored_rel_err(h, rh)
+    return max(ey, eh)
 
 
-def f32_gate(inp, flags=0) -> float:
+def f32_gate(inp, flags=0, err_y=None, err_h=None) -> float:
     """fp32 gate of one scan case: 1e-5, raised to 1.5x the case's emulated fp32
     floor where fp32 arithmetic itself is above 2/3 of it."""
-    return max(PLAIN_F32_GATE, FLOOR_MARGIN * emulated_floor(inp, flags))
+    return max(PLAIN_F32_GATE, FLOOR_MARGIN * emulated_floor(inp, flags, err_y=err_y, err_h=err_h))
 
 
-def decode_f32_gate(inp, steps, flags=0) -> float:
+def decode_f32_gate(inp, steps, flags=0, err_y=None, err_h=None) -> float:
     """f32_gate for `steps` decode steps from a zero state: the same updates as a
     scan over those steps (update == scan step, pinned on the CPU)."""
     seq = {k: np.ascontiguousarray(inp[k][:steps].transpose(1, 0, 2)) for k in ("x", "delta", "z", "B", "C")}
     seq.update(A=inp["A"], D=inp["D"], dt_bias=inp["dt_bias"],
                h0=np.zeros((seq["x"].shape[0], seq["x"].shape[2], inp["A"].shape[1]), np.float32))
-    return f32_gate(seq, flags)
+    return f32_gate(seq, flags, err_y=err_y, err_h=err_h)
 
 
 def _floor(shape, seed, params, softplus=False, zoh=False, ideal_softplus=False):
