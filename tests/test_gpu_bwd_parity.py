@@ -16,12 +16,14 @@ pytestmark = pytest.mark.gpu
 SP = 0x1  # SSM_FLAG_DELTA_SOFTPLUS
 ZOH = 0x2  # SSM_FLAG_EXACT_ZOH
 
-# Gates on the floored relative error of every gradient.  fp32 io: sized by
-# the float32 emulation in test_tolerance_bwd.py (ddelta's fp32 floor grows
-# with the memory of slow channels: up to ~1.2e-4 on ~1000-step cases with a
-# 1-ulp exp2); bf16 io: dx, ddelta and dz are rounded to bf16 (2^-9
-# relative), as for y.
-from test_tolerance_bwd import BWD_F32_GATE as F32_GATE  # noqa: E402
+# Gates on the floored relative error of every gradient.  fp32 io: per
+# gradient, sized by the float32 emulation in test_tolerance_bwd.py (ddelta's
+# fp32 floor grows with the memory of slow channels: up to ~1.2e-4 on
+# ~1000-step cases with a 1-ulp exp2, gate 5e-4 for it and d_dt_bias; the
+# other gradients stay within 3.4e-5, gate 1.5e-4); bf16 io: dx, ddelta and dz
+# are rounded to bf16 (2^-9 relative), as for y.
+from test_tolerance_bwd import bwd_f32_gate  # noqa: E402
+F32_GATE = "f32"  # per gradient: bwd_f32_gate
 BF16_GATE = 2e-2
 
 
@@ -65,7 +67,8 @@ def _compare(g, r, gate, keys=None, label=""):
         errs[k] = floored_rel_err(g[k], r[k]) if r[k].size else 0.0
     print(label, " ".join("%s %.2e" % kv for kv in errs.items()), flush=True)
     for k, e in errs.items():
-        assert e <= gate, (k, e)
+        gk = bwd_f32_gate(k) if gate == F32_GATE else gate
+        assert e <= gk, (k, e, gk)
     return errs
 
 
@@ -191,7 +194,7 @@ def test_bwd_exact_zoh(lib, dtype, softplus, d_state):
     _compare(g, r, _gate(dtype), label="zoh %s sp=%d N=%d" % (dtype, softplus, d_state))
     # The plain-step gradient differs from it at a visible level: the case sees the mode.
     plain = _ref(inp, gr, softplus=softplus)
-    assert floored_rel_err(plain["dA"], r["dA"]) > 10 * _gate(dtype)
+    assert floored_rel_err(plain["dA"], r["dA"]) > 10 * (bwd_f32_gate("dA") if dtype == "f32" else BF16_GATE)
 
 
 @pytest.mark.parametrize("fwd_ckpt", [False, True])

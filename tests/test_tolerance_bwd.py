@@ -12,8 +12,11 @@ remember and the two terms cancel more and more.  On ~1000-step cases the
 emulation with correctly rounded exp2 reaches 4e-5 to 7e-5; with each exp2
 result off by a random -1, 0 or +1 ulp (the accuracy of the hardware's
 v_exp_f32) it reaches up to ~1.2e-4.  BWD_F32_GATE = 5e-4 leaves 4x room over
-that model; every other gradient stays near 1e-5.  A real mistake (a dropped
-term, a decay from the wrong step) costs percent-level errors.
+that model; it gates ddelta and the dt_bias gradient (a sum of ddelta's
+terms).  Every other gradient stays within 3.4e-5 in the same model (dA with
+the exact ZOH, dh0 on a 1000-step case), so BWD_F32_GATE_REST = 1.5e-4 gates
+them with the same 4x room.  A real mistake (a dropped term, a decay from the wrong
+step) costs percent-level errors.
 
 The emulation is test-side arithmetic only (neither the oracle nor the device
 path); it restates the fp32 steps of the kernel for one purpose: to size the
@@ -25,7 +28,13 @@ import oracle
 from conftest import floored_rel_err
 from selective_state_space_84_amd import inputs
 
-BWD_F32_GATE = 5e-4
+BWD_F32_GATE = 5e-4        # ddelta and d_dt_bias (cancellation in ddelta's two terms)
+BWD_F32_GATE_REST = 1.5e-4  # every other gradient
+
+
+def bwd_f32_gate(name: str) -> float:
+    """fp32-io gate of one gradient (floored relative error)."""
+    return BWD_F32_GATE if name in ("ddelta", "d_dt_bias") else BWD_F32_GATE_REST
 
 f = np.float32
 L2E = f(1.4426950408889634)
@@ -142,9 +151,10 @@ def test_backward_fp32_floor_sizes_the_gate():
     emu = _emulate_bwd(inp, gr)
     errs = {k: floored_rel_err(emu[k], ref[k]) for k in emu}
     print(" ".join("%s %.2e" % kv for kv in errs.items()))
-    # The emulation itself sits well below the gate, with room for the
-    # hardware's transcendentals and summation orders ...
-    assert max(errs.values()) <= BWD_F32_GATE / 2
+    # The emulation itself sits well below each gradient's gate, with room
+    # for the hardware's transcendentals and summation orders ...
+    for k, e in errs.items():
+        assert e <= bwd_f32_gate(k) / 2, (k, e)
     # ... and ddelta is the gradient that needs the looser gate: plain fp32
     # arithmetic in this order already exceeds the forward's 1e-5.
     assert errs["ddelta"] > 1e-5
@@ -164,8 +174,8 @@ def test_backward_fp32_floor_with_hardware_exp2_model():
         emu = _emulate_bwd(inp, gr, exp2=_exp2_1ulp)
         errs = {k: floored_rel_err(emu[k], ref[k]) for k in emu}
         print("trial", trial, " ".join("%s %.2e" % kv for kv in errs.items()))
-        worst = max(worst, max(errs.values()))
-    assert worst <= BWD_F32_GATE / 3
+        worst = max(worst, max(e / bwd_f32_gate(k) for k, e in errs.items()))
+    assert worst <= 1 / 3
 
 
 def test_backward_fp32_floor_exact_zoh():
@@ -180,7 +190,8 @@ def test_backward_fp32_floor_exact_zoh():
     emu = _emulate_bwd(inp, gr, exp2=_exp2_1ulp, exact_zoh=True)
     errs = {k: floored_rel_err(emu[k], ref[k]) for k in emu}
     print(" ".join("%s %.2e" % kv for kv in errs.items()))
-    assert max(errs.values()) <= BWD_F32_GATE / 3
+    for k, e in errs.items():
+        assert e <= bwd_f32_gate(k) / 3, (k, e)
     # The emulation without the exact ZOH is far off: the check sees the mode.
     plain = _emulate_bwd(inp, gr)
     assert floored_rel_err(plain["dA"], ref["dA"]) > 1e-2
