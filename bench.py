@@ -18,6 +18,10 @@ line also carries, each as its own object:
   * the scan's backward pass, the causal conv1d, the decode update (256 x
     5120 x 16 state, 1000 in-place steps), the Mamba-2 SSD form, and the fp64
     CPU oracle on a bounded sample of the headline workload (cpu_baseline).
+The oracle (test infrastructure under oracle/) is used only by the
+cpu_baseline leg: its timed sample, and the whole-row comparisons of GPU
+outputs with it (the parity objects above).  --no-cpu-baseline skips that
+leg entirely, and then nothing under oracle/ is loaded.
 Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -292,8 +296,16 @@ def oracle_rows(cfg, inp, rows, flags=0, width=256):
     return out
 
 
+# False with --no-cpu-baseline: the oracle leg (its timing and every whole-row
+# comparison with it) is skipped.
+_ORACLE_LEG = True
+
+
 def row_parity(cfg, inp, y, hl, rows, flags=0):
-    """Floored errors of whole GPU rows against the oracle."""
+    """Floored errors of whole GPU rows against the oracle (part of the
+    cpu_baseline leg)."""
+    if not _ORACLE_LEG:
+        return {"skipped": "--no-cpu-baseline"}
     ref = oracle_rows(cfg, inp, rows, flags)
     ey = max(_floored(_host_f64(y[b]), ref[b][0]) for b in rows)
     eh = max(_floored(_host_f64(hl[b]), ref[b][1]) for b in rows)
@@ -621,6 +633,8 @@ def main():
     ap.add_argument("--flags", default="",
                     help="comma list: softplus (fused softplus step), zoh (exact ZOH), linear (structured A)")
     args = ap.parse_args()
+    global _ORACLE_LEG
+    _ORACLE_LEG = not args.no_cpu_baseline
     _settle_ms[0] = max(0.0, args.settle_ms)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
