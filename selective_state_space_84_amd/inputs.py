@@ -457,3 +457,39 @@ def make_degenerate(inp: Dict[str, np.ndarray], seed: int, raw_delta: bool = Fal
     D[1::5] = -D[1::5]
     out["A"], out["D"] = A, D
     return out
+
+
+def make_degenerate_ssd(inp: Dict[str, np.ndarray], seed: int, raw_dt: bool = False) -> Dict[str, np.ndarray]:
+    """make_degenerate for the scalar-decay (SSD) inputs of make_ssd_inputs:
+    per (row, step, head) 5% zero steps (raw -100 with ``raw_dt``) and 3%
+    steps of 30 (raw 40) with that head's x row set to 1/32; x = 0 on 3% of
+    the other elements; z = 60, -60, -200 on 3% of elements each; 6% of the
+    (row, step, group) B rows and of the C rows zero; A = 0 (no decay) on the
+    first head; D = 0 on every 3rd head and negated on the next.  Positions
+    from ``SeedSequence([seed, 0xDE7]).spawn(4)`` = [step, x, z, rows]."""
+    ks, kx, kz, kr = np.random.SeedSequence([seed, 0xDE7]).spawn(4)
+    out = dict(inp)
+    x, dt, z = (_io_values(inp[k]) for k in ("x", "dt", "z"))
+    B, C = _io_values(inp["B"]), _io_values(inp["C"])
+    u = np.random.default_rng(ks).random(dt.shape)
+    dt[u < 0.05] = -100.0 if raw_dt else 0.0
+    big = (u >= 0.05) & (u < 0.08)
+    dt[big] = 40.0 if raw_dt else 30.0
+    x[big] = 1.0 / 32.0
+    x[(np.random.default_rng(kx).random(x.shape) < 0.03) & ~big[..., None]] = 0.0
+    v = np.random.default_rng(kz).random(z.shape)
+    z[v < 0.03] = 60.0
+    z[(v >= 0.03) & (v < 0.06)] = -60.0
+    z[(v >= 0.06) & (v < 0.09)] = -200.0
+    rows = np.random.default_rng(kr).random((2,) + B.shape[:3])
+    B[rows[0] < 0.06] = 0.0
+    C[rows[1] < 0.06] = 0.0
+    for k, val in (("x", x), ("dt", dt), ("z", z), ("B", B), ("C", C)):
+        out[k] = _like_io(val, inp[k])
+    A = inp["A"].copy()
+    A[0] = 0.0
+    D = inp["D"].copy()
+    D[::3] = 0.0
+    D[1::3] = -D[1::3]
+    out["A"], out["D"] = A, D
+    return out

@@ -85,3 +85,17 @@ def test_degenerate_values_are_planted(dtype, raw_delta):
     # general inputs also get single zero states
     gen = inputs.make_degenerate(inputs.make_scan_inputs(1, 10, 30, 16, dtype, 3), 3)
     assert np.all(gen["A"][::7, 2] == 0.0)
+
+
+def test_degenerate_ssd_values_are_planted():
+    inp = inputs.make_ssd_inputs(2, 100, 4, 64, 1, 64, 7, nonzero_h0=True, params="random")
+    deg = inputs.make_degenerate_ssd(inp, 7)
+    dt, x, z = (inputs._io_values(deg[k]) for k in ("dt", "x", "z"))
+    assert 0.03 < np.mean(dt == 0.0) < 0.07 and 0.015 < np.mean(dt == 30.0) < 0.045
+    assert np.all(x[dt == 30.0] == 1.0 / 32.0)
+    for v in (60.0, -60.0, -200.0):
+        assert 0.015 < np.mean(z == v) < 0.045, v
+    assert 0.01 < np.all(inputs._io_values(deg["B"]) == 0.0, axis=-1).mean() < 0.15
+    assert deg["A"][0] == 0.0 and np.all(deg["A"][1:] == inp["A"][1:])
+    assert deg["D"][0] == 0.0 and deg["D"][1] == -inp["D"][1]
+    assert np.array_equal(inputs._io_values(inp["dt"]) == 0.0, np.zeros(inp["dt"].shape, bool))

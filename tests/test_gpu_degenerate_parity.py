@@ -10,7 +10,8 @@ zeros, D = 0 or negative, and gate inputs far into both tails of SiLU (z =
 -200 makes e^-z overflow fp32; the gate is then -0).  Every entry point of
 the recurrence meets them: the scan in every launch plan (unsplit, state
 split over lanes, sequence chunks), the structured-A path, the softplus and
-exact-ZOH step modes, the decode update and the backward pass.  Gates as
+exact-ZOH step modes, the decode update, the backward pass and the
+scalar-decay (SSD) form (inputs.make_degenerate_ssd).  Gates as
 elsewhere: fp32 io 1e-5 or the case's emulated fp32 floor
 (test_tolerance_floor.f32_gate), bf16 io 2e-2; the backward's gates from
 test_tolerance_bwd.  The planted values widen the outputs' range (a gate
@@ -167,3 +168,33 @@ def test_bwd_degenerate_values(lib, flags, dtype):
         assert np.isfinite(g[k]).all(), k
         gate = bwd_f32_gate(k) if dtype == "f32" else 2e-2
         assert e <= gate, (k, e, gate)
+
+
+@pytest.mark.parametrize("d_state,ngroups,softplus", [(64, 1, False), (128, 2, False), (64, 2, True)])
+def test_ssd_degenerate_values(lib, d_state, ngroups, softplus):
+    """The scalar-decay (SSD) form on the same kinds of degenerate values
+    (inputs.make_degenerate_ssd): zero steps, steps of 30 that wipe the state
+    (the kept state's scale resets), a head with A = 0, zero B/C rows, gate
+    tails, D = 0 or negative; 150 steps (four full 32-step chunks and a
+    ragged one).  bf16 io: gate 2e-2 per class."""
+    import torch
+    from gpu_util import to_dev, to_host_f64
+    seed = 8700 + d_state + ngroups + softplus
+    inp = inputs.make_ssd_inputs(2, 150, 4, 64, ngroups, d_state, seed, nonzero_h0=True, raw_dt=softplus,
+                                 params="random")
+    inp = inputs.make_degenerate_ssd(inp, seed, raw_dt=softplus)
+    print("case degenerate ssd", d_state, ngroups, softplus, flush=True)
+    d = {k: to_dev(inp.get(k)) for k in ("x", "dt", "A", "B", "C", "D", "z", "h0", "dt_bias")}
+    y, hl = binding.ssm_ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
+                                flags=SP if softplus else 0, dt_bias=d["dt_bias"] if softplus else None)
+    torch.cuda.synchronize()
+    ry, rh = oracle.ssd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
+                        inp["dt_bias"] if softplus else None, delta_softplus=softplus)
+    gy, gh = to_host_f64(y), to_host_f64(hl)
+    assert np.isfinite(gy).all() and np.isfinite(gh).all()
+    tail = np.abs(inputs._io_values(inp["z"])) >= 50.0
+    undamped = np.broadcast_to((inp["A"] == 0.0)[None, :, None, None], rh.shape)
+    ey = _class_err(gy, ry, [tail, ~tail])
+    eh = _class_err(gh, rh, [undamped, ~undamped])
+    print("  errors y %.2e h %.2e" % (ey, eh), flush=True)
+    assert ey <= 2e-2 and eh <= 2e-2, (ey, eh)
